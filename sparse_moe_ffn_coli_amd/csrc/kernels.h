@@ -1,0 +1,48 @@
+// kernels.h -- internal launch interface between the C ABI (api.hip) and the
+// kernels (route.hip, ffn.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coli {
+
+struct RouteLaunch {
+    int T, D, E, K;
+    bool bf16;
+    const void *x;
+    const void *wr;
+    const float *bias;
+    float *z;              // workspace [T][E]
+    int32_t *tile_count;   // workspace [ceil(T/64)][E]
+    int32_t *tile_base;    // workspace [ceil(T/64)][E]
+    int32_t *ids;
+    float *w;
+    int32_t *count, *offset, *perm, *inv;
+};
+
+struct FfnLaunch {
+    int T, D, E, K, F;
+    bool bf16;
+    int bm;                // tile height of the grouped GEMMs (bf16)
+    const void *x;
+    const int32_t *ids;
+    const float *w;
+    const int32_t *count, *offset, *perm, *inv;
+    const void *gate, *up, *down, *s_gate, *s_up, *s_down;
+    const float *residual;
+    float *y;
+    void *y_bf16;
+    void *h;               // workspace [T*K + T][F]
+    void *o;               // workspace [T*K][D]
+    int2 *tiles;           // workspace [ffn_max_tiles]
+    int32_t *n_tiles;      // workspace [2]
+};
+
+hipError_t launch_route(const RouteLaunch &a, hipStream_t st);
+hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st);
+
+int ffn_tile_rows(int T, int E, int K);
+long ffn_max_tiles(int T, int E, int K, int bm);
+
+}  // namespace coli

@@ -1,0 +1,97 @@
+"""Helpers for the GPU parity tests: run the HIP layer through the C ABI on
+seeded inputs and compare with the oracle.
+
+Tolerances (bf16/int4 from the workload definition, fp32 likewise):
+  ids, count, offset, perm, inv   bit-exact
+  routing weights w               max |w - w_ref| <= 1e-4
+  y                               max |y - y_ref| / rms(y_ref) <= 1e-4 (fp32) or 2e-2 (bf16, int4)
+"""
+import math
+
+import numpy as np
+
+import oracle
+import synth
+from sparse_moe_ffn_coli_amd import COLI_BF16, COLI_F32
+from sparse_moe_ffn_coli_amd.layer import DeviceLayer, to_device
+
+TOL_Y = {"f32": 1e-4, "bf16": 2e-2}
+TOL_W = 1e-4
+
+
+def custom_cfg(cid, T, D, E, K, F, dtype="bf16", bias="uniform", int4=False, group=32):
+    return dict(cid=cid, T=T, D=D, E=E, K=K, F=F, dtype=dtype, bias=bias, layers=1,
+                int4=int4, group=group)
+
+
+def make_inputs(cfg, attempts=None, seed=0):
+    W = synth.layer_weights(cfg, 0, seed)
+    W["x"] = synth.x_rows(cfg, attempts, 0, seed)
+    return W
+
+
+def gpu_layer(W, cfg, device="cuda"):
+    dt = COLI_F32 if cfg["dtype"] == "f32" else COLI_BF16
+    layer = DeviceLayer(W, cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], dt, device=device,
+                        group=cfg.get("group", 32))
+    x = to_device(W["x"], device)
+    return layer, x
+
+
+def run_gpu(W, cfg, device="cuda"):
+    import torch
+    layer, x = gpu_layer(W, cfg, device)
+    y = layer(x)
+    torch.cuda.synchronize()
+    out = layer.routing_numpy()
+    out["y"] = y.cpu().numpy().astype(np.float64)
+    return out
+
+
+def _oracle_mats(W):
+    if "gate_q" in W:
+        G = W.get("group", 32)
+        return (oracle.Mat.int4(W["gate_q"], W["gate_s"], G),
+                oracle.Mat.int4(W["up_q"], W["up_s"], G),
+                oracle.Mat.int4(W["down_q"], W["down_s"], G))
+    return W["gate"], W["up"], W["down"]
+
+
+def run_oracle(W, cfg, tokens=None):
+    g, u, d = _oracle_mats(W)
+    return oracle.moe_layer(W["x"], W["wr"], W["bias"], g, u, d, W["s_gate"], W["s_up"],
+                            W["s_down"], cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"],
+                            tokens=tokens)
+
+
+def compare(got, ref, cfg, tokens=None, label=""):
+    """Assert parity; returns a dict of the measured errors."""
+    for k in ("ids", "count", "offset", "perm", "inv"):
+        if not np.array_equal(got[k], ref[k]):
+            bad = np.nonzero(got[k].reshape(-1) != ref[k].reshape(-1))[0]
+            raise AssertionError(f"{label}: {k} differs at {len(bad)} positions, first {bad[:8]}")
+    werr = float(np.abs(got["w"] - ref["w"]).max()) if got["w"].size else 0.0
+    assert werr <= TOL_W, f"{label}: max |dw| = {werr:.3e}"
+    y = got["y"] if tokens is None else got["y"][np.asarray(tokens)]
+    yref = ref["y"]
+    rms = math.sqrt(float(np.mean(yref ** 2))) if yref.size else 1.0
+    yerr = float(np.abs(y - yref).max()) / rms if yref.size else 0.0
+    tol = TOL_Y["f32" if cfg["dtype"] == "f32" else "bf16"]
+    assert np.all(np.isfinite(y)), f"{label}: non-finite outputs"
+    assert yerr <= tol, f"{label}: max|dy|/rms = {yerr:.3e} > {tol}"
+    return dict(w_err=werr, y_err=yerr)
+
+
+def sample_tokens(ids, count, T, n_random=24, seed=0):
+    """First/last tokens, tokens of the most and least loaded experts, random ones."""
+    rng = np.random.default_rng(seed)
+    picks = {0, T - 1}
+    nonempty = np.nonzero(count)[0]
+    hot = int(np.argmax(count))
+    cold = nonempty[np.argsort(count[nonempty], kind="stable")[:4]]
+    for e in [hot, *cold.tolist()]:
+        toks = np.nonzero((ids == e).any(axis=1))[0]
+        picks.update(toks[:2].tolist())
+        picks.update(toks[-1:].tolist())
+    picks.update(rng.choice(T, min(n_random, T), replace=False).tolist())
+    return np.array(sorted(picks), dtype=np.int64)

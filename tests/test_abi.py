@@ -1,0 +1,141 @@
+"""CPU checks of the C ABI library: it loads, exports every function that
+include/coli_moe.h declares, sizes workspaces, and rejects invalid arguments
+on the host before any device work (fake device addresses are used; none is
+ever dereferenced because every case fails validation first)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import sparse_moe_ffn_coli_amd as pkg
+from sparse_moe_ffn_coli_amd import (COLI_BF16, COLI_F32, CRouting, CShape, CWeights,
+                                     CWeightsInt4)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coli_moe.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WS, E_DEVICE, E_LAUNCH, E_ALIAS = range(9)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coli_moe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pkg.lib()
+    names = declared_functions()
+    assert set(names) >= {"coli_moe_route", "coli_moe_ffn", "coli_moe_ffn_int4",
+                          "coli_moe_workspace_bytes", "coli_moe_status_str"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(pkg.EXPORTED)
+
+
+def test_status_strings():
+    for code in range(9):
+        s = pkg.coli_moe_status_str(code)
+        assert isinstance(s, str) and s
+    assert pkg.coli_moe_status_str(0) == "ok"
+    assert pkg.coli_moe_version() >= 100
+
+
+def _shape(T=64, D=2048, E=288, K=8, F=768, dt=COLI_BF16):
+    return pkg.Shape(T, D, E, K, F, dt)
+
+
+def test_workspace_sizes():
+    s = _shape()
+    n = pkg.coli_moe_workspace_bytes(s)
+    R = 64 * 8
+    assert n >= (R + 64) * 768 * 2 + R * 2048 * 2          # h and o in bf16
+    assert pkg.coli_moe_workspace_bytes(_shape(T=4096)) > n
+    assert pkg.coli_moe_workspace_bytes(_shape(K=9)) == 0   # invalid shape -> 0
+    assert pkg.coli_moe_workspace_bytes(_shape(T=0)) > 0
+
+
+# fake, 256-aligned device addresses; never dereferenced
+BASE = 0x7F0000000000
+
+
+def fake(i, misalign=0):
+    return BASE + i * (1 << 32) + misalign
+
+
+def _routing(misalign=0):
+    return CRouting(*(fake(20 + i, misalign if i == 0 else 0) for i in range(6)))
+
+
+def _route(shape, x=fake(1), wr=fake(2), bias=fake(3), routing=None, ws=fake(4), ws_bytes=1 << 31):
+    routing = routing if routing is not None else _routing()
+    cs = shape if isinstance(shape, CShape) else shape.c()
+    return pkg.lib().coli_moe_route(C.byref(cs), x, wr, bias, C.byref(routing), ws, ws_bytes, None)
+
+
+def _weights(misalign=0):
+    return CWeights(*(fake(40 + i, misalign if i == 2 else 0) for i in range(6)))
+
+
+def _ffn(shape, x=fake(1), routing=None, w=None, residual=None, y=fake(5), y_bf16=None,
+         ws=fake(4), ws_bytes=1 << 31):
+    routing = routing if routing is not None else _routing()
+    w = w if w is not None else _weights()
+    cs = shape.c()
+    return pkg.lib().coli_moe_ffn(C.byref(cs), x, C.byref(routing), C.byref(w), residual, y,
+                                  y_bf16, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), E_SHAPE), (dict(K=9), E_SHAPE), (dict(E=7), E_SHAPE), (dict(E=1025), E_SHAPE),
+    (dict(D=100), E_SHAPE), (dict(F=96), E_SHAPE), (dict(T=-1), E_SHAPE), (dict(D=0), E_SHAPE),
+    (dict(dt=2), E_DTYPE)])
+def test_route_rejects_bad_shapes(kw, code):
+    assert _route(_shape(**kw)) == code
+
+
+def test_route_rejects_null_misaligned_small_workspace():
+    assert pkg.lib().coli_moe_route(None, fake(1), fake(2), fake(3), C.byref(_routing()),
+                                    fake(4), 1 << 31, None) == E_NULL
+    assert _route(_shape(), x=None) == E_NULL
+    assert _route(_shape(), bias=None) == E_NULL
+    assert _route(_shape(), routing=CRouting(0, 0, 0, 0, 0, 0)) == E_NULL
+    assert _route(_shape(), x=fake(1, 2)) == E_ALIGN
+    assert _route(_shape(), routing=_routing(misalign=8)) == E_ALIGN
+    assert _route(_shape(), ws_bytes=16) == E_WS
+
+
+def test_ffn_rejects_bad_arguments():
+    s = _shape()
+    assert _ffn(_shape(K=0)) == E_SHAPE
+    assert _ffn(s, y=None) == E_NULL
+    assert _ffn(s, w=CWeights(0, 0, 0, 0, 0, 0)) == E_NULL
+    assert _ffn(s, w=_weights(misalign=4)) == E_ALIGN
+    assert _ffn(s, residual=fake(6, 8)) == E_ALIGN
+    assert _ffn(_shape(dt=COLI_F32), y_bf16=fake(7)) == E_DTYPE     # bf16 copy of an fp32 layer
+    assert _ffn(s, y=fake(1) + 1024) == E_ALIAS                      # y inside x
+    assert _ffn(s, y_bf16=fake(5) + 4096) == E_ALIAS                 # y_bf16 inside y
+    assert _ffn(s, residual=fake(5) + 256) == E_ALIAS                # partial overlap with y
+    assert _ffn(s, ws_bytes=1000) == E_WS
+
+
+def test_int4_rejects_fp32_and_null():
+    cs = _shape(dt=COLI_F32).c()
+    w = CWeightsInt4(*([fake(50 + i) for i in range(6)] + [32] + [fake(60 + i) for i in range(3)]))
+    assert pkg.lib().coli_moe_ffn_int4(C.byref(cs), fake(1), C.byref(_routing()), C.byref(w),
+                                       None, fake(5), None, fake(4), 1 << 31, None) == E_DTYPE
+    cs2 = _shape().c()
+    assert pkg.lib().coli_moe_ffn_int4(C.byref(cs2), fake(1), C.byref(_routing()), None,
+                                       None, fake(5), None, fake(4), 1 << 31, None) == E_NULL
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    # Only meaningful on a host with no GPU: there the last host check, the
+    # device query, fails.  Never run it where a GPU could receive the fake
+    # addresses.
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake addresses must not reach it")
+    assert _route(_shape()) == E_DEVICE
+    assert _ffn(_shape()) == E_DEVICE

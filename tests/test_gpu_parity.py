@@ -1,0 +1,145 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
+inputs: small shapes that span several tiles with ragged tails, the full
+workloads (prefill on sampled tokens), edge cases, and run-to-run bitwise
+determinism.  Tolerances are in gpu_helpers."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import (compare, custom_cfg, gpu_layer, make_inputs, run_gpu, run_oracle,
+                         sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_moe_ffn_coli_amd as pkg
+    pkg.lib()
+
+
+def _report(label, err):
+    print(f"{label}: ids/perm bit-exact, w_err={err['w_err']:.2e}, y_err={err['y_err']:.2e}",
+          flush=True)
+
+
+# ---------------------------------------------------------------------------
+# small shapes: several tiles, ragged tails, full oracle
+# ---------------------------------------------------------------------------
+SMALL = [
+    # cid, T, D, E, K, F, dtype  -- rows per expert decide the tile height
+    (101, 200, 256, 40, 8, 192, "bf16"),     # 40 rows/expert: 128-row tiles, ragged
+    (102, 100, 128, 288, 8, 128, "bf16"),    # ~3 rows/expert: 16-row tiles
+    (103, 67, 192, 24, 8, 64, "f32"),
+    (104, 130, 64, 16, 8, 64, "bf16"),       # minimum widths, heavy load per expert
+]
+
+
+@pytest.mark.parametrize("cid,T,D,E,K,F,dt", SMALL)
+def test_small_shapes(cid, T, D, E, K, F, dt):
+    cfg = custom_cfg(cid, T, D, E, K, F, dt)
+    W = make_inputs(cfg)
+    got = run_gpu(W, cfg)
+    ref = run_oracle(W, cfg)
+    _report(f"small cid={cid}", compare(got, ref, cfg, label=f"cid={cid}"))
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------
+def test_tiny_fp32():
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.workload("tiny")
+    _report("tiny", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="tiny"))
+
+
+def test_decode_bf16():
+    cfg = synth.CONFIGS["decode"]
+    W = synth.workload("decode")
+    _report("decode", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="decode"))
+
+
+def test_prefill_bf16_sampled():
+    import oracle
+    cfg = synth.CONFIGS["prefill"]
+    W = synth.workload("prefill")
+    got = run_gpu(W, cfg)
+    T, D, E, K = cfg["T"], cfg["D"], cfg["E"], cfg["K"]
+    # routing of every token from the oracle, the FFN for a sample
+    z = oracle.router_logits(W["x"], W["wr"], W["bias"], T, D, E)
+    ids, w = oracle.select_topk(z, K)
+    count, offset, perm, inv = oracle.permutation(ids, E)
+    assert (count == 0).sum() > 0
+    toks = sample_tokens(ids, count, T)
+    y = oracle.moe_ffn(W["x"], ids, w, W["gate"], W["up"], W["down"], W["s_gate"], W["s_up"],
+                       W["s_down"], T, D, E, K, cfg["F"], tokens=toks)
+    ref = dict(ids=ids, w=w, count=count, offset=offset, perm=perm, inv=inv, y=y)
+    err = compare(got, ref, cfg, tokens=toks, label="prefill")
+    _report(f"prefill ({len(toks)} sampled tokens, {(count > 0).sum()} non-empty experts)", err)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cid,T,D,E,K,F,dt", [
+    (111, 1, 128, 288, 8, 64, "bf16"),       # a single token
+    (112, 9, 64, 8, 8, 64, "bf16"),          # E = K: every expert chosen by every token
+    (113, 33, 128, 50, 1, 64, "bf16"),       # K = 1
+    (114, 70, 64, 1024, 8, 64, "bf16"),      # the largest supported E
+    (115, 5, 64, 8, 8, 64, "f32"),
+])
+def test_edge_shapes(cid, T, D, E, K, F, dt):
+    cfg = custom_cfg(cid, T, D, E, K, F, dt)
+    W = make_inputs(cfg)
+    _report(f"edge cid={cid}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label=f"cid={cid}"))
+
+
+def test_zero_tokens():
+    import torch
+    cfg = custom_cfg(120, 0, 64, 16, 8, 64, "bf16")
+    W = make_inputs(cfg)
+    layer, x = gpu_layer(W, cfg)
+    layer.routing.count.fill_(7)
+    layer.routing.offset.fill_(7)
+    layer(x)
+    torch.cuda.synchronize()
+    assert layer.routing.count.cpu().tolist() == [0] * 16
+    assert layer.routing.offset.cpu().tolist() == [0] * 17
+
+
+def test_residual_and_bf16_output():
+    import torch
+    cfg = custom_cfg(121, 80, 128, 32, 8, 64, "bf16")
+    W = make_inputs(cfg)
+    layer, x = gpu_layer(W, cfg)
+    y0 = layer(x).clone()
+    res = torch.randn_like(y0)
+    y = res.clone()
+    yb = torch.empty(y0.shape, dtype=torch.bfloat16, device=y0.device)
+    layer.ffn(x, y=y, residual=y, y_bf16=yb)          # in place: y = y + layer(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, res + y0)
+    assert torch.equal(yb, y.to(torch.bfloat16))
+
+
+# ---------------------------------------------------------------------------
+# determinism: identical inputs give bitwise identical routing and outputs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_bitwise_determinism(name):
+    import torch
+    cfg = synth.CONFIGS[name]
+    W = synth.workload(name)
+    layer, x = gpu_layer(W, cfg)
+    outs = []
+    for _ in range(3):
+        y = layer(x).clone()
+        torch.cuda.synchronize()
+        r = layer.routing_numpy()
+        outs.append((y.cpu().numpy(), r))
+    for y, r in outs[1:]:
+        assert np.array_equal(y.view(np.uint32), outs[0][0].view(np.uint32))
+        for k in r:
+            assert np.array_equal(r[k], outs[0][1][k])
