@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE FFN layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch: coli_moe_route
+(router GEMM, top-8, permutation) + coli_moe_ffn (grouped gate+up with the
+clamped SwiGLU, grouped down, shared expert + fixed-order combine), inputs
+resident in HBM.  The default workload is the T=4096 prefill batch (bf16,
+Zipf-skewed router bias); the T=64 decode batch is measured as well and
+reported under "decode".
+
+Prints ONE JSON line.  Besides the throughput it reports
+  roofline:     the dominant kernel (gate+up) against its bound, from HIP
+                events recorded around that kernel inside the timed region;
+  cpu_baseline: the CPU oracle timed on a bounded sample of the same inputs.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|int4|tiny]
+"""
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_FP32_FLOPS = 157.3e12   # MI355X fp32 vector
+PEAK_HBM = 8.0e12            # MI355X HBM3E bytes/s
+
+WORKLOAD_NAMES = {
+    "prefill": "prefill T=4096, D=2048, F=768, 288 experts top-8 + 1 shared, bf16, Zipf(1.1) router bias",
+    "decode": "decode T=64, D=2048, F=768, 288 experts top-8 + 1 shared, bf16",
+    "int4": "int4 experts T=512, D=2048, F=768, 288 experts top-8 + 1 shared, group 32",
+    "tiny": "tiny T=8, D=128, F=64, 288 experts top-8 + 1 shared, fp32",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime's C API (recorded by the library itself on
+# the stream its kernels run on)
+# ---------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        self.L = C.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.L.hipEventDestroy.argtypes = [C.c_void_p]
+        self.L.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = C.c_void_p()
+            assert self.L.hipEventCreate(C.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.L.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = C.c_float()
+        assert self.L.hipEventSynchronize(b) == 0
+        assert self.L.hipEventElapsedTime(C.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.L.hipEventDestroy(e)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one step (per stage), from the realised routing
+# ---------------------------------------------------------------------------
+def algorithmic(cfg, count, int4=False):
+    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
+    R = T * K
+    n_e = int((count > 0).sum())
+    act = 4 if cfg["dtype"] == "f32" else 2              # activation / dense weight bytes
+    if int4:
+        G = cfg["group"]
+        wbytes = lambda rows, k: rows * k // 2 + rows * (k // G) * 2
+    else:
+        wbytes = lambda rows, k: rows * k * act
+    gu_w = n_e * 2 * wbytes(F, D) + 2 * F * D * act       # routed (non-empty) + shared gate/up
+    dn_w = n_e * wbytes(D, F)
+    sd_w = D * F * act
+    st = {
+        "router": dict(flops=2 * T * D * E, bytes=E * D * act + T * D * act + T * E * 4),
+        "gate_up": dict(flops=2 * (R + T) * D * 2 * F,
+                        bytes=gu_w + T * D * act + (R + T) * F * act),
+        "down": dict(flops=2 * R * F * D, bytes=dn_w + R * F * act + R * D * act),
+        "combine": dict(flops=2 * T * F * D + 2 * R * D,
+                        bytes=sd_w + T * F * act + R * D * act + T * D * 4),
+    }
+    total_flops = sum(s["flops"] for s in st.values())
+    # whole-step algorithmic bytes: every weight that must be read once, x in, y out
+    total_bytes = (E * D * act + gu_w + dn_w + sd_w + T * D * act + T * D * 4)
+    return st, total_flops, total_bytes, n_e
+
+
+def roofline(flops, nbytes, seconds, peak_flops):
+    t_mfma, t_hbm = flops / peak_flops, nbytes / PEAK_HBM
+    if t_mfma >= t_hbm:
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": peak_flops / 1e12,
+                "unit": "TFLOP/s", "frac": round(a * 1e12 / peak_flops, 4)}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(a * 1e9 / PEAK_HBM, 4)}
+
+
+# ---------------------------------------------------------------------------
+# one workload on the GPU
+# ---------------------------------------------------------------------------
+def run_workload(name, steps, warmup, hip):
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_moe_ffn_coli_amd import COLI_BF16, COLI_F32, FFN_STAGES, ROUTE_STAGES
+    from sparse_moe_ffn_coli_amd.layer import DeviceLayer, to_device
+
+    cfg = synth.CONFIGS[name]
+    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
+    t0 = time.time()
+    W = synth.workload(name)
+    log(f"{name}: generated inputs in {time.time() - t0:.1f}s")
+    dt = COLI_F32 if cfg["dtype"] == "f32" else COLI_BF16
+    layer = DeviceLayer(W, T, D, E, K, F, dt, group=cfg.get("group", 32))
+    x = to_device(W["x"])
+    del W
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    for _ in range(warmup):
+        layer(x)
+    torch.cuda.synchronize()
+    log(f"{name}: {warmup} warm-up steps done")
+
+    # timed region: K steps; the library records events around the gate+up
+    # kernel of every step (ffn stage 1) on the stream it launches on
+    gu = hip.events(2 * steps)
+    start, stop = hip.events(2)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    hip.record(start, stream)
+    for i in range(steps):
+        layer(x, ffn_events=[None, gu[2 * i], gu[2 * i + 1]])
+    hip.record(stop, stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    total_ms = hip.elapsed_ms(start, stop)
+    gu_ms = [hip.elapsed_ms(gu[2 * i], gu[2 * i + 1]) for i in range(steps)]
+    log(f"{name}: {steps} timed steps, {total_ms / steps * 1e3:.1f} us/step "
+        f"(host clock {host_s / steps * 1e6:.1f} us/step)")
+
+    # per-stage breakdown (diagnostic, outside the timed region)
+    n_r, n_f = len(ROUTE_STAGES) + 1, len(FFN_STAGES) + 1
+    evs = hip.events((n_r + n_f) * steps)
+    for i in range(steps):
+        b = evs[(n_r + n_f) * i:(n_r + n_f) * (i + 1)]
+        layer(x, route_events=b[:n_r], ffn_events=b[n_r:])
+    torch.cuda.synchronize()
+    stage_us = {}
+    for j, nm in enumerate(ROUTE_STAGES):
+        stage_us[nm] = sum(hip.elapsed_ms(evs[(n_r + n_f) * i + j], evs[(n_r + n_f) * i + j + 1])
+                           for i in range(steps)) / steps * 1e3
+    for j, nm in enumerate(FFN_STAGES):
+        o = n_r
+        stage_us[nm] = sum(hip.elapsed_ms(evs[(n_r + n_f) * i + o + j],
+                                          evs[(n_r + n_f) * i + o + j + 1])
+                           for i in range(steps)) / steps * 1e3
+    hip.destroy(gu + evs + [start, stop])
+
+    count = layer.routing.count.cpu().numpy()
+    st, flops, nbytes, n_e = algorithmic(cfg, count, int4=cfg.get("int4", False))
+    step_s = total_ms / steps / 1e3
+    gu_s = sum(gu_ms) / len(gu_ms) / 1e3
+    peak = PEAK_FP32_FLOPS if cfg["dtype"] == "f32" else PEAK_BF16_FLOPS
+    res = dict(
+        cfg=cfg, step_s=step_s, host_step_s=host_s / steps, tokens_per_s=T / step_s, n_e=n_e,
+        flops=flops, bytes=nbytes, gu_s=gu_s, stage_us={k: round(v, 2) for k, v in stage_us.items()},
+        roofline=roofline(st["gate_up"]["flops"], st["gate_up"]["bytes"], gu_s, peak),
+        gate_up_work=st["gate_up"],
+        mfma_pct=round(100 * flops / step_s / peak, 2),
+        hbm_gbs=round(nbytes / step_s / 1e9, 1),
+        hbm_pct=round(100 * nbytes / step_s / PEAK_HBM, 2),
+    )
+    del layer, x
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+def cpu_baseline(name, budget_s=15.0):
+    import numpy as np
+
+    import oracle
+    import synth
+
+    cfg = synth.CONFIGS[name]
+    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
+    W = synth.workload(name)
+    if cfg.get("int4"):
+        G = cfg["group"]
+        g = oracle.Mat.int4(W["gate_q"], W["gate_s"], G)
+        u = oracle.Mat.int4(W["up_q"], W["up_s"], G)
+        d = oracle.Mat.int4(W["down_q"], W["down_s"], G)
+    else:
+        g, u, d = W["gate"], W["up"], W["down"]
+
+    def run(n):
+        xs = np.ascontiguousarray(W["x"][:n])
+        t = time.perf_counter()
+        oracle.moe_layer(xs, W["wr"], W["bias"], g, u, d, W["s_gate"], W["s_up"], W["s_down"],
+                         n, D, E, K, F)
+        return time.perf_counter() - t
+
+    threads = oracle.num_threads()
+    probe = min(T, max(threads, 8))
+    tp = run(probe)
+    n = int(min(T, max(probe, budget_s / max(tp / probe, 1e-9))))
+    n = max(probe, (n // threads) * threads) if n >= threads else n
+    el = run(n) if n != probe else tp
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of the {T} tokens of the {name} workload: router over all "
+                      f"{E} experts, top-{K}, routed + shared FFN, in fp64 ({el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    import sparse_moe_ffn_coli_amd as pkg
+    pkg.lib()
+    hip = Hip()
+
+    main_res = run_workload(args.workload, args.steps, args.warmup, hip)
+    dec = None
+    if args.workload == "prefill" and not args.no_decode:
+        dec = run_workload("decode", args.steps, args.warmup, hip)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(args.workload)
+        log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} threads")
+
+    cfg = main_res["cfg"]
+    out = {
+        "metric": f"routed-MoE tokens/s ({args.workload})" if args.workload != "prefill"
+                  else "routed-MoE tokens/s at T=4096 prefill",
+        "value": round(main_res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["step_s"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg["dtype"] == "f32" else "bf16",
+        "data": "synthetic (seeded generator, seed 0)",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "global_batch": cfg["T"],
+                   "seq_len": 1, "parallelism": "none (one GPU)", "experts": cfg["E"],
+                   "top_k": cfg["K"], "d_model": cfg["D"], "d_ff": cfg["F"],
+                   "nonempty_experts": main_res["n_e"]},
+        "roofline": dict(main_res["roofline"], traffic=None, kernel="gate_up",
+                         avg_us=round(main_res["gu_s"] * 1e6, 2)),
+        "mfma_pct": main_res["mfma_pct"],
+        "hbm_gbs": main_res["hbm_gbs"],
+        "hbm_pct": main_res["hbm_pct"],
+        "stage_us": main_res["stage_us"],
+        "cpu_baseline": cpu,
+    }
+    if dec is not None:
+        out["decode"] = {"tokens_per_s": round(dec["tokens_per_s"], 1),
+                         "ms_per_step": round(dec["step_s"] * 1e3, 4),
+                         "hbm_gbs": dec["hbm_gbs"], "hbm_pct": dec["hbm_pct"],
+                         "nonempty_experts": dec["n_e"], "roofline": dec["roofline"],
+                         "stage_us": dec["stage_us"]}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -36,8 +36,9 @@
  *   - Layouts are row-major with the reduction index contiguous:
  *       x [T][D], W_router [E][D], gate/up [E][F][D], down [E][D][F],
  *       shared gate/up [F][D], shared down [D][F], y [T][D].
- *   - Every pointer must be 16-byte aligned.  T = 0 is valid and enqueues
- *     nothing.
+ *   - Every pointer must be 16-byte aligned.  T = 0 is valid: routing then
+ *     writes zero counts and offsets and the FFN enqueues nothing (the
+ *     per-assignment routing arrays may be NULL).
  *   - Results are bitwise reproducible run to run for the same inputs and
  *     shape (no floating-point atomics; every reduction has a fixed order).
  */
@@ -148,6 +149,29 @@ coli_status coli_moe_ffn_int4(const coli_moe_shape *s, const void *x,
                               const coli_moe_routing *r, const coli_moe_weights_int4 *w,
                               const float *residual, float *y, void *y_bf16, void *ws,
                               size_t ws_bytes, void *stream);
+
+/* Instrumented variants for timing each kernel of a call: the same work and
+ * bitwise the same results as the plain entry points, and in addition the
+ * caller's HIP events (hipEvent_t handles passed as void*) are recorded on
+ * `stream`: events[i] just before stage i is enqueued and events[n_stages]
+ * after the last one.  Entries past n_events, and NULL entries, are skipped.
+ * Nothing is recorded when the call fails validation or T = 0.
+ *   route stages (5): router logits, top-K, tile histogram, scan, scatter
+ *   ffn stages (4):   tile list, gate+up (+SwiGLU), down, shared down + combine
+ *                     (the fp32 path has no tile list: events 0 and 1 coincide) */
+coli_status coli_moe_route_timed(const coli_moe_shape *s, const void *x, const void *w_router,
+                                 const float *bias, const coli_moe_routing *out, void *ws,
+                                 size_t ws_bytes, void *stream, void *const *events,
+                                 int32_t n_events);
+coli_status coli_moe_ffn_timed(const coli_moe_shape *s, const void *x, const coli_moe_routing *r,
+                               const coli_moe_weights *w, const float *residual, float *y,
+                               void *y_bf16, void *ws, size_t ws_bytes, void *stream,
+                               void *const *events, int32_t n_events);
+coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
+                                    const coli_moe_routing *r, const coli_moe_weights_int4 *w,
+                                    const float *residual, float *y, void *y_bf16, void *ws,
+                                    size_t ws_bytes, void *stream, void *const *events,
+                                    int32_t n_events);
 
 /* Static description of a status code. */
 const char *coli_moe_status_str(coli_status st);

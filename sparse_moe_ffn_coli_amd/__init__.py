@@ -32,7 +32,10 @@ STATUS_NAMES = {0: "COLI_OK", 1: "COLI_E_NULL", 2: "COLI_E_SHAPE", 3: "COLI_E_DT
                 4: "COLI_E_ALIGN", 5: "COLI_E_WORKSPACE", 6: "COLI_E_DEVICE",
                 7: "COLI_E_LAUNCH", 8: "COLI_E_ALIAS"}
 EXPORTED = ("coli_moe_workspace_bytes", "coli_moe_route", "coli_moe_ffn", "coli_moe_ffn_int4",
+            "coli_moe_route_timed", "coli_moe_ffn_timed", "coli_moe_ffn_int4_timed",
             "coli_moe_status_str", "coli_moe_version")
+ROUTE_STAGES = ("router", "topk", "perm_hist", "perm_scan", "perm_scatter")
+FFN_STAGES = ("tiles", "gate_up", "down", "combine")
 
 
 class ColiError(RuntimeError):
@@ -91,6 +94,13 @@ def lib():
         L.coli_moe_ffn_int4.restype = C.c_int
         L.coli_moe_ffn_int4.argtypes = [sp, vp, C.POINTER(CRouting), C.POINTER(CWeightsInt4),
                                         vp, vp, vp, vp, sz, vp]
+        ev = C.POINTER(C.c_void_p)
+        L.coli_moe_route_timed.restype = C.c_int
+        L.coli_moe_route_timed.argtypes = L.coli_moe_route.argtypes + [ev, C.c_int32]
+        L.coli_moe_ffn_timed.restype = C.c_int
+        L.coli_moe_ffn_timed.argtypes = L.coli_moe_ffn.argtypes + [ev, C.c_int32]
+        L.coli_moe_ffn_int4_timed.restype = C.c_int
+        L.coli_moe_ffn_int4_timed.argtypes = L.coli_moe_ffn_int4.argtypes + [ev, C.c_int32]
         L.coli_moe_status_str.restype = C.c_char_p
         L.coli_moe_status_str.argtypes = [C.c_int]
         L.coli_moe_version.restype = C.c_int32
@@ -215,27 +225,49 @@ def coli_moe_workspace_bytes(shape: Shape, int4: bool = False) -> int:
     return lib().coli_moe_workspace_bytes(C.byref(cs), 1 if int4 else 0)
 
 
+def _nbytes(ws, ws_bytes):
+    if ws_bytes is not None:
+        return ws_bytes
+    return ws.numel() * ws.element_size() if ws is not None else 0
+
+
+def _events(events):
+    """A list of hipEvent_t handles (ints) -> (void** array, count); None -> (None, 0)."""
+    if not events:
+        return None, 0
+    arr = (C.c_void_p * len(events))(*events)
+    return arr, len(events)
+
+
 def coli_moe_route(shape: Shape, x, w_router, bias, routing: Routing, ws, ws_bytes=None,
-                   stream=None) -> None:
+                   stream=None, events=None) -> None:
+    """Route T tokens; ``events`` (hipEvent_t handles) selects the timed variant."""
     cs, cr = shape.c(), routing.c()
-    nbytes = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(lib().coli_moe_route(C.byref(cs), _ptr(x), _ptr(w_router), _ptr(bias), C.byref(cr),
-                                _ptr(ws), nbytes, _stream(stream)), "coli_moe_route")
+    args = [C.byref(cs), _ptr(x), _ptr(w_router), _ptr(bias), C.byref(cr), _ptr(ws),
+            _nbytes(ws, ws_bytes), _stream(stream)]
+    if events:
+        _check(lib().coli_moe_route_timed(*args, *_events(events)), "coli_moe_route_timed")
+    else:
+        _check(lib().coli_moe_route(*args), "coli_moe_route")
 
 
 def coli_moe_ffn(shape: Shape, x, routing: Routing, weights: Weights, y, residual=None,
-                 y_bf16=None, ws=None, ws_bytes=None, stream=None) -> None:
+                 y_bf16=None, ws=None, ws_bytes=None, stream=None, events=None) -> None:
     cs, cr, cw = shape.c(), routing.c(), weights.c()
-    nbytes = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(lib().coli_moe_ffn(C.byref(cs), _ptr(x), C.byref(cr), C.byref(cw), _ptr(residual),
-                              _ptr(y), _ptr(y_bf16), _ptr(ws), nbytes, _stream(stream)),
-           "coli_moe_ffn")
+    args = [C.byref(cs), _ptr(x), C.byref(cr), C.byref(cw), _ptr(residual), _ptr(y),
+            _ptr(y_bf16), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)]
+    if events:
+        _check(lib().coli_moe_ffn_timed(*args, *_events(events)), "coli_moe_ffn_timed")
+    else:
+        _check(lib().coli_moe_ffn(*args), "coli_moe_ffn")
 
 
 def coli_moe_ffn_int4(shape: Shape, x, routing: Routing, weights: WeightsInt4, y, residual=None,
-                      y_bf16=None, ws=None, ws_bytes=None, stream=None) -> None:
+                      y_bf16=None, ws=None, ws_bytes=None, stream=None, events=None) -> None:
     cs, cr, cw = shape.c(), routing.c(), weights.c()
-    nbytes = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(lib().coli_moe_ffn_int4(C.byref(cs), _ptr(x), C.byref(cr), C.byref(cw),
-                                   _ptr(residual), _ptr(y), _ptr(y_bf16), _ptr(ws), nbytes,
-                                   _stream(stream)), "coli_moe_ffn_int4")
+    args = [C.byref(cs), _ptr(x), C.byref(cr), C.byref(cw), _ptr(residual), _ptr(y),
+            _ptr(y_bf16), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)]
+    if events:
+        _check(lib().coli_moe_ffn_int4_timed(*args, *_events(events)), "coli_moe_ffn_int4_timed")
+    else:
+        _check(lib().coli_moe_ffn_int4(*args), "coli_moe_ffn_int4")

@@ -92,10 +92,13 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn)
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
-coli_status check_routing(const coli_moe_routing *r)
+// With T = 0 the per-assignment arrays are empty and may be NULL; count and
+// offset always exist.
+coli_status check_routing(const coli_moe_routing *r, int32_t T)
 {
     if (!r) return COLI_E_NULL;
-    if (!r->ids || !r->w || !r->count || !r->offset || !r->perm || !r->inv) return COLI_E_NULL;
+    if (!r->count || !r->offset) return COLI_E_NULL;
+    if (T > 0 && (!r->ids || !r->w || !r->perm || !r->inv)) return COLI_E_NULL;
     if (!aligned16(r->ids) || !aligned16(r->w) || !aligned16(r->count) || !aligned16(r->offset) ||
         !aligned16(r->perm) || !aligned16(r->inv))
         return COLI_E_ALIGN;
@@ -135,9 +138,17 @@ coli_status coli_moe_route(const coli_moe_shape *s, const void *x, const void *w
                            const float *bias, const coli_moe_routing *out, void *ws,
                            size_t ws_bytes, void *stream)
 {
+    return coli_moe_route_timed(s, x, w_router, bias, out, ws, ws_bytes, stream, nullptr, 0);
+}
+
+coli_status coli_moe_route_timed(const coli_moe_shape *s, const void *x, const void *w_router,
+                                 const float *bias, const coli_moe_routing *out, void *ws,
+                                 size_t ws_bytes, void *stream, void *const *events,
+                                 int32_t n_events)
+{
     coli_status st = check_shape(s);
     if (st != COLI_OK) return st;
-    if ((st = check_routing(out)) != COLI_OK) return st;
+    if ((st = check_routing(out, s->T)) != COLI_OK) return st;
     if (s->T > 0 && (!x || !w_router || !bias || !ws)) return COLI_E_NULL;
     if (!aligned16(x) || !aligned16(w_router) || !aligned16(bias) || !aligned16(ws)) return COLI_E_ALIGN;
     const RouteWs L = route_ws(s);
@@ -154,6 +165,8 @@ coli_status coli_moe_route(const coli_moe_shape *s, const void *x, const void *w
     a.tile_base = (int32_t *)(base + L.tile_base);
     a.ids = out->ids; a.w = out->w; a.count = out->count; a.offset = out->offset;
     a.perm = out->perm; a.inv = out->inv;
+    coli::StageMarks marks{events, n_events, 0};
+    a.marks = &marks;
     return coli::launch_route(a, (hipStream_t)stream) == hipSuccess ? COLI_OK : COLI_E_LAUNCH;
 }
 
@@ -162,7 +175,7 @@ static coli_status ffn_common_checks(const coli_moe_shape *s, const void *x, con
                                      size_t ws_bytes, size_t need)
 {
     coli_status st;
-    if ((st = check_routing(r)) != COLI_OK) return st;
+    if ((st = check_routing(r, s->T)) != COLI_OK) return st;
     if (!x || !y || !ws) return COLI_E_NULL;
     if (!aligned16(x) || !aligned16(y) || !aligned16(ws) || (residual && !aligned16(residual)) ||
         (y_bf16 && !aligned16(y_bf16)))
@@ -182,6 +195,14 @@ static coli_status ffn_common_checks(const coli_moe_shape *s, const void *x, con
 coli_status coli_moe_ffn(const coli_moe_shape *s, const void *x, const coli_moe_routing *r,
                          const coli_moe_weights *w, const float *residual, float *y, void *y_bf16,
                          void *ws, size_t ws_bytes, void *stream)
+{
+    return coli_moe_ffn_timed(s, x, r, w, residual, y, y_bf16, ws, ws_bytes, stream, nullptr, 0);
+}
+
+coli_status coli_moe_ffn_timed(const coli_moe_shape *s, const void *x, const coli_moe_routing *r,
+                               const coli_moe_weights *w, const float *residual, float *y,
+                               void *y_bf16, void *ws, size_t ws_bytes, void *stream,
+                               void *const *events, int32_t n_events)
 {
     coli_status st = check_shape(s);
     if (st != COLI_OK) return st;
@@ -209,6 +230,8 @@ coli_status coli_moe_ffn(const coli_moe_shape *s, const void *x, const coli_moe_
     a.h = base + L.h; a.o = base + L.o;
     a.tiles = (int2 *)(base + L.tiles);
     a.n_tiles = (int32_t *)(base + L.n_tiles);
+    coli::StageMarks marks{events, n_events, 0};
+    a.marks = &marks;
     return coli::launch_ffn(a, (hipStream_t)stream) == hipSuccess ? COLI_OK : COLI_E_LAUNCH;
 }
 
@@ -216,6 +239,17 @@ coli_status coli_moe_ffn_int4(const coli_moe_shape *s, const void *x, const coli
                               const coli_moe_weights_int4 *w, const float *residual, float *y,
                               void *y_bf16, void *ws, size_t ws_bytes, void *stream)
 {
+    return coli_moe_ffn_int4_timed(s, x, r, w, residual, y, y_bf16, ws, ws_bytes, stream, nullptr,
+                                   0);
+}
+
+coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
+                                    const coli_moe_routing *r, const coli_moe_weights_int4 *w,
+                                    const float *residual, float *y, void *y_bf16, void *ws,
+                                    size_t ws_bytes, void *stream, void *const *events,
+                                    int32_t n_events)
+{
+    (void)events; (void)n_events;
     (void)x; (void)r; (void)residual; (void)y; (void)y_bf16; (void)ws; (void)ws_bytes; (void)stream;
     coli_status st = check_shape(s);
     if (st != COLI_OK) return st;

@@ -326,45 +326,56 @@ long ffn_max_tiles(int T, int E, int K, int bm)
 }
 
 template <class C>
-static void launch_bf16_gemms(const FfnLaunch &a, hipStream_t st)
+static void launch_bf16_gemms(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
     const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
     const uint16_t *h = (const uint16_t *)a.h;
+    mk.mark(st);
     gateup_bf16_kernel<C><<<(unsigned)(mt * (a.F / (C::BN / 2))), 256, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
         (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.tiles,
         a.n_tiles, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     const int n_nt_d = (a.D + C::BN - 1) / C::BN;
+    mk.mark(st);
     down_bf16_kernel<C><<<(unsigned)(mt * n_nt_d), 256, 0, st>>>(
         h, (const uint16_t *)a.down, a.count, a.offset, a.tiles, a.n_tiles, a.D, a.F,
         (uint16_t *)a.o);
     const int n_mt = (a.T + C::BM - 1) / C::BM;
+    mk.mark(st);
     combine_bf16_kernel<C><<<(unsigned)(n_mt * n_nt_d), 256, 0, st>>>(
         h, (const uint16_t *)a.s_down, (const uint16_t *)a.o, a.w, a.inv, a.residual, a.T, a.D, a.K,
         a.F, a.y, (uint16_t *)a.y_bf16);
+    mk.mark(st);
 }
 
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
 {
     const int T = a.T, D = a.D, K = a.K, F = a.F;
     const int R = T * K;
+    StageMarks none;
+    StageMarks &mk = a.marks ? *a.marks : none;
+    mk.mark(st);
     if (a.bf16) {
         ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, T, a.bm, a.tiles, a.n_tiles);
         if (a.bm == 16)
-            launch_bf16_gemms<Cfg16>(a, st);
+            launch_bf16_gemms<Cfg16>(a, mk, st);
         else
-            launch_bf16_gemms<Cfg128>(a, st);
+            launch_bf16_gemms<Cfg128>(a, mk, st);
     } else {
         const int64_t n1 = (int64_t)(R + T) * F, n2 = (int64_t)R * D, n3 = (int64_t)T * D;
+        mk.mark(st);
         gateup_f32_kernel<<<(unsigned)((n1 + 255) / 256), 256, 0, st>>>(
             (const float *)a.x, (const float *)a.gate, (const float *)a.up, (const float *)a.s_gate,
             (const float *)a.s_up, a.ids, a.perm, T, D, K, F, (float *)a.h);
+        mk.mark(st);
         if (n2 > 0)
             down_f32_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, st>>>(
                 (const float *)a.h, (const float *)a.down, a.ids, a.perm, R, D, F, (float *)a.o);
+        mk.mark(st);
         combine_f32_kernel<<<(unsigned)((n3 + 255) / 256), 256, 0, st>>>(
             (const float *)a.h, (const float *)a.s_down, (const float *)a.o, a.w, a.inv, a.residual, T,
             D, K, F, a.y);
+        mk.mark(st);
     }
     return hipGetLastError();
 }

@@ -7,6 +7,18 @@
 
 namespace coli {
 
+// Records caller-owned events between stages (instrumented entry points).
+struct StageMarks {
+    void *const *ev = nullptr;
+    int n = 0;
+    int next = 0;
+    void mark(hipStream_t st)
+    {
+        if (ev && next < n && ev[next]) (void)hipEventRecord((hipEvent_t)ev[next], st);
+        ++next;
+    }
+};
+
 struct RouteLaunch {
     int T, D, E, K;
     bool bf16;
@@ -19,6 +31,7 @@ struct RouteLaunch {
     int32_t *ids;
     float *w;
     int32_t *count, *offset, *perm, *inv;
+    StageMarks *marks;     // nullable
 };
 
 struct FfnLaunch {
@@ -37,6 +50,7 @@ struct FfnLaunch {
     void *o;               // workspace [T*K][D]
     int2 *tiles;           // workspace [ffn_max_tiles]
     int32_t *n_tiles;      // workspace [2]
+    StageMarks *marks;     // nullable
 };
 
 hipError_t launch_route(const RouteLaunch &a, hipStream_t st);

@@ -277,6 +277,9 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
         route_empty_kernel<<<1, 256, 0, st>>>(E, a.count, a.offset);
         return hipGetLastError();
     }
+    StageMarks none;
+    StageMarks &mk = a.marks ? *a.marks : none;
+    mk.mark(st);
     if (a.bf16) {
         int n_nt = (E + RouterCfg::BN - 1) / RouterCfg::BN;
         int n_mt = (T + RouterCfg::BM - 1) / RouterCfg::BM;
@@ -287,11 +290,16 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
         router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
             (const float *)a.x, (const float *)a.wr, a.bias, T, D, E, a.z);
     }
+    mk.mark(st);
     topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
     const int ntiles = (T + 63) / 64;
+    mk.mark(st);
     perm_hist_kernel<<<ntiles, 64, 0, st>>>(a.ids, T, E, K, a.tile_count);
+    mk.mark(st);
     perm_scan_kernel<<<1, 1024, 0, st>>>(a.tile_count, ntiles, E, a.tile_base, a.count, a.offset);
+    mk.mark(st);
     perm_scatter_kernel<<<ntiles, 64, 0, st>>>(a.ids, T, E, K, a.tile_base, a.perm, a.inv);
+    mk.mark(st);
     return hipGetLastError();
 }
 

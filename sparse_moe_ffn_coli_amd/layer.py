@@ -48,22 +48,24 @@ class DeviceLayer:
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         self.y = torch.empty((T, D), dtype=torch.float32, device=device)
 
-    def route(self, x, stream=None):
-        coli_moe_route(self.shape, x, self.wr, self.bias, self.routing, self.ws, stream=stream)
+    def route(self, x, stream=None, events=None):
+        coli_moe_route(self.shape, x, self.wr, self.bias, self.routing, self.ws, stream=stream,
+                       events=events)
 
-    def ffn(self, x, y=None, residual=None, y_bf16=None, stream=None):
+    def ffn(self, x, y=None, residual=None, y_bf16=None, stream=None, events=None):
         y = self.y if y is None else y
         if self.int4:
             coli_moe_ffn_int4(self.shape, x, self.routing, self.weights, y, residual=residual,
-                              y_bf16=y_bf16, ws=self.ws, stream=stream)
+                              y_bf16=y_bf16, ws=self.ws, stream=stream, events=events)
         else:
             coli_moe_ffn(self.shape, x, self.routing, self.weights, y, residual=residual,
-                         y_bf16=y_bf16, ws=self.ws, stream=stream)
+                         y_bf16=y_bf16, ws=self.ws, stream=stream, events=events)
         return y
 
-    def __call__(self, x, y=None, residual=None, y_bf16=None, stream=None):
-        self.route(x, stream)
-        return self.ffn(x, y, residual, y_bf16, stream)
+    def __call__(self, x, y=None, residual=None, y_bf16=None, stream=None, route_events=None,
+                 ffn_events=None):
+        self.route(x, stream, route_events)
+        return self.ffn(x, y, residual, y_bf16, stream, ffn_events)
 
     def routing_numpy(self) -> dict:
         r = self.routing
