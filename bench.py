@@ -16,7 +16,10 @@ Prints ONE JSON line.  Besides the throughput it reports
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|int4|tiny]
 """
 import argparse
+import csv
 import ctypes as C
+import glob
+import hashlib
 import json
 import math
 import os
@@ -40,6 +43,88 @@ WORKLOAD_NAMES = {
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel from rocprofv3 counters
+#
+# Two counter runs of the same command (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch) are scaled by what the same counters read for a plain device copy
+# of known size (--copy-calibration, 256 MiB read + 256 MiB written), and
+# stored with a hash of the kernel sources.  The bench reports the traffic
+# only while the sources still hash the same.
+# ---------------------------------------------------------------------------
+KERNEL_SOURCES = ("sparse_moe_ffn_coli_amd/csrc/ffn.hip", "sparse_moe_ffn_coli_amd/csrc/route.hip",
+                  "sparse_moe_ffn_coli_amd/csrc/device_common.h")
+COPY_BYTES = 256 << 20
+
+
+def sources_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {COPY_BYTES >> 20} MiB device copy x3")
+
+
+def _pmc_values(folder, counter):
+    """kernel name -> list of per-dispatch counter values"""
+    out = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, out_path, workload, command):
+    fetch, write = _pmc_values(fetch_dir, "FETCH_SIZE"), _pmc_values(write_dir, "WRITE_SIZE")
+    # the calibration copies are the largest dispatches of the runtime's copy kernel
+    copy = next(k for k in fetch if "copyBuffer" in k)
+    f_scale = COPY_BYTES / (max(fetch[copy]) * 1024.0)
+    w_scale = COPY_BYTES / (max(write[copy]) * 1024.0)
+    kernels = {}
+    for k, v in fetch.items():
+        if not k.startswith("void coli::") and not k.startswith("coli::"):
+            continue
+        fk = sum(v) / len(v)
+        wk = sum(write.get(k, [0.0])) / len(write.get(k, [0.0]))
+        short = k.split("(")[0].replace("void ", "")
+        kernels[short] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "dispatches": len(v),
+                          "hbm_bytes": round(fk * 1024 * f_scale + wk * 1024 * w_scale)}
+    summary = {"workload": workload, "command": command, "sources_sha256_16": sources_hash(),
+               "copy_kernel": copy.split("(")[0], "copy_bytes_each_way": COPY_BYTES,
+               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": kernels}
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1, sort_keys=True)
+    print(json.dumps(summary, indent=1, sort_keys=True))
+
+
+def recorded_traffic(workload, kernel_prefix):
+    """HBM bytes per launch of the kernel from the committed counter summary, or
+    None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        summ = json.load(f)
+    if summ.get("sources_sha256_16") != sources_hash():
+        return None
+    for name, v in summ["kernels"].items():
+        if name.split("::")[-1].startswith(kernel_prefix):
+            return v["hbm_bytes"]
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -246,7 +331,15 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 256 MiB device copy first (scale for counter runs)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                    help="turn two rocprofv3 --pmc runs into a traffic summary and exit")
+    ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, workload=args.workload, command=args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
@@ -257,6 +350,8 @@ def main():
     import sparse_moe_ffn_coli_amd as pkg
     pkg.lib()
     hip = Hip()
+    if args.copy_calibration:
+        copy_calibration()
 
     main_res = run_workload(args.workload, args.steps, args.warmup, hip)
     dec = None
@@ -287,8 +382,10 @@ def main():
                    "seq_len": 1, "parallelism": "none (one GPU)", "experts": cfg["E"],
                    "top_k": cfg["K"], "d_model": cfg["D"], "d_ff": cfg["F"],
                    "nonempty_experts": main_res["n_e"]},
-        "roofline": dict(main_res["roofline"], traffic=None, kernel="gate_up",
-                         avg_us=round(main_res["gu_s"] * 1e6, 2)),
+        "roofline": dict(main_res["roofline"], traffic=recorded_traffic(args.workload, "gateup"),
+                         kernel="gate_up", avg_us=round(main_res["gu_s"] * 1e6, 2),
+                         algorithmic_bytes=main_res["gate_up_work"]["bytes"],
+                         algorithmic_flops=main_res["gate_up_work"]["flops"]),
         "mfma_pct": main_res["mfma_pct"],
         "hbm_gbs": main_res["hbm_gbs"],
         "hbm_pct": main_res["hbm_pct"],

@@ -37,7 +37,7 @@ struct RouteWs {
     size_t z, tile_count, tile_base, total;
 };
 struct FfnWs {
-    size_t h, o, tiles, n_tiles, total;
+    size_t h, o, list_gu, list_dn, n_items, total;
     int bm;
 };
 
@@ -45,7 +45,7 @@ RouteWs route_ws(const coli_moe_shape *s)
 {
     RouteWs w{};
     const size_t T = (size_t)s->T, E = (size_t)s->E;
-    const size_t ntiles = (T + 63) / 64;
+    const size_t ntiles = (size_t)coli::perm_tiles(s->T);
     w.z = 0;
     w.tile_count = align_up(w.z + T * E * 4);
     w.tile_base = align_up(w.tile_count + ntiles * E * 4);
@@ -64,9 +64,10 @@ FfnWs ffn_ws(const coli_moe_shape *s, int int4)
     const size_t max_tiles = (size_t)coli::ffn_max_tiles(s->T, s->E, s->K, w.bm);
     w.h = 0;
     w.o = align_up(w.h + (R + T) * F * elt);
-    w.tiles = align_up(w.o + R * D * elt);
-    w.n_tiles = align_up(w.tiles + max_tiles * 8);
-    w.total = align_up(w.n_tiles + 16);
+    w.list_gu = align_up(w.o + R * D * elt);
+    w.list_dn = align_up(w.list_gu + max_tiles * (size_t)coli::ffn_col_tiles_gu(s->F) * 16);
+    w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * 16);
+    w.total = align_up(w.n_items + 16);
     return w;
 }
 
@@ -228,8 +229,9 @@ coli_status coli_moe_ffn_timed(const coli_moe_shape *s, const void *x, const col
     a.residual = residual; a.y = y; a.y_bf16 = y_bf16;
     char *base = (char *)ws;
     a.h = base + L.h; a.o = base + L.o;
-    a.tiles = (int2 *)(base + L.tiles);
-    a.n_tiles = (int32_t *)(base + L.n_tiles);
+    a.list_gu = (int4 *)(base + L.list_gu);
+    a.list_dn = (int4 *)(base + L.list_dn);
+    a.n_items = (int32_t *)(base + L.n_items);
     coli::StageMarks marks{events, n_events, 0};
     a.marks = &marks;
     return coli::launch_ffn(a, (hipStream_t)stream) == hipSuccess ? COLI_OK : COLI_E_LAUNCH;

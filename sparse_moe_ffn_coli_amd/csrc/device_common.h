@@ -43,42 +43,69 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u)
 }
 
 // ---------------------------------------------------------------------------
+// Wave-wide reductions on DPP lane permutations (no LDS traffic): within each
+// row of 16 lanes, quad swaps, then the half-row and row mirrors; the four
+// row results are then combined through readlane.  Every lane returns the
+// result.
+// ---------------------------------------------------------------------------
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op)
+{
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+struct MaxU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+struct MinU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+
+// ---------------------------------------------------------------------------
 // bf16 MFMA tile engine
 //
 // A workgroup of 256 threads (4 waves of 64) computes a BM x BN block of
 // C = A * B^T with A [BM][K] and B [BN][K] both K-contiguous (every matrix
 // product of the layer has this form: activations times weight rows).  K is
 // walked in steps of BK = 64: each step's A and B tiles are copied from
-// global memory into LDS (16-byte chunks, one row = 8 chunks, chunk c of row
-// r stored at position c ^ (r & 7) to spread MFMA operand reads over the
-// banks), double-buffered so the global loads of step k+1 are in flight
-// while step k runs on the matrix cores.  The waves form a WAVES_M x WAVES_N
-// grid; each wave owns FM x FN fragments of 16x16 and issues
-// v_mfma_f32_16x16x32_bf16 on them.
+// global memory into LDS (16-byte chunks, one row = 8 chunks), double-buffered
+// so the global loads of step k+1 are in flight while step k runs on the
+// matrix cores.  The waves form a WAVES_M x WAVES_N grid; each wave owns
+// FM x FN fragments of 32x32 and issues v_mfma_f32_32x32x16_bf16 on them
+// (on gfx950 this instruction delivers twice the bf16 rate of the 16x16x32
+// form, measured 2.36 vs 1.24 PFLOP/s).
 //
-// Fragment layouts of v_mfma_f32_16x16x32_bf16 (lane l, i = 0..3):
-//   A operand: row (l & 15), reduction slots 8*(l >> 4) .. +7
-//   B operand: col (l & 15), the same reduction slots
-//   result   : row 4*(l >> 4) + i, col (l & 15)
+// Fragment layouts of v_mfma_f32_32x32x16_bf16 (lane l, i = 0..15):
+//   A operand: row (l & 31), reduction slots 8*(l >> 5) .. +7
+//   B operand: col (l & 31), the same reduction slots
+//   result   : row 8*(i >> 2) + 4*(l >> 5) + (i & 3), col (l & 31)
 // A and B take the same slots from the same K positions, so the pairing of
 // products is exact whatever the hardware's slot order.
 //
+// LDS layout: chunk c of row r sits at chunk position c ^ ((r >> 1) & 7).
+// A fragment read covers 16 lanes = 16 consecutive rows of one logical
+// chunk per LDS cycle; with 128-byte rows, even and odd rows fall in
+// different bank halves and the XOR spreads each half's 8 rows over 8
+// distinct chunk positions, so reads and the row-pair writes are free of
+// bank conflicts.
+//
 // Rows are supplied as per-thread source pointers (gathered activation rows,
-// expert weight rows), one per load chunk of the thread, including chunks
-// past the tile (rows >= BM or >= BN), which are loaded and dropped.  Every
-// pointer must be a readable row: a padding row
-// (past an expert's last token, past the weight matrix's last row) points at
-// any valid row instead.  Row m of the result depends only on row m of A and
-// column n only on row n of B, so padding rows only reach results that the
-// caller discards.
+// expert weight rows), one per load chunk of the thread.  Every pointer must
+// be a readable row: a padding row (past an expert's last token, past the
+// weight matrix's last row) points at any valid row instead.  Row m of the
+// result depends only on row m of A and column n only on row n of B, so
+// padding rows only reach results that the caller discards.
 // ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NT = 256;
     static constexpr int BK = 64;
-    static constexpr int FM = BM / (WAVES_M * 16);
-    static constexpr int FN = BN / (WAVES_N * 16);
+    static constexpr int FM = BM / (WAVES_M * 32);
+    static constexpr int FN = BN / (WAVES_N * 32);
     static constexpr int A_CHUNKS = BM * BK / 8;
     static constexpr int B_CHUNKS = BN * BK / 8;
     static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
@@ -87,23 +114,36 @@ struct TileCfg {
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
     static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
     static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid");
-    static_assert(BM % (WAVES_M * 16) == 0 && BN % (WAVES_N * 16) == 0, "tile shape");
+    static_assert(BM % (WAVES_M * 32) == 0 && BN % (WAVES_N * 32) == 0, "tile shape");
 };
 
 // Index (in bf16 elements) of chunk `ch` of row `row` inside one tile region.
 __device__ __forceinline__ int swz(int row, int ch)
 {
-    return (row * 8 + (ch ^ (row & 7))) * 8;
+    return (row * 8 + (ch ^ ((row >> 1) & 7))) * 8;
 }
 
 // Row of this thread's i-th load chunk (the chunk column is tid & 7 for all i).
 template <class C>
 __device__ __forceinline__ int a_chunk_row(int i) { return (threadIdx.x + i * C::NT) >> 3; }
 
+// Row (within the tile) and column of accumulator element i of fragment
+// (m, n) for this lane.
+template <class C>
+__device__ __forceinline__ int acc_row(int wm, int m, int lane, int i)
+{
+    return (wm * C::FM + m) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+template <class C>
+__device__ __forceinline__ int acc_col(int wn, int n, int lane)
+{
+    return (wn * C::FN + n) * 32 + (lane & 31);
+}
+
 template <class C>
 __device__ __forceinline__ void mfma_mainloop(const uint16_t *const (&ap)[C::A_PER_T],
                                               const uint16_t *const (&bp)[C::B_PER_T], int K,
-                                              uint16_t *lds, f32x4 (&acc)[C::FM][C::FN])
+                                              uint16_t *lds, f32x16 (&acc)[C::FM][C::FN])
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -141,42 +181,212 @@ __device__ __forceinline__ void mfma_mainloop(const uint16_t *const (&ap)[C::A_P
     for (int m = 0; m < C::FM; ++m)
 #pragma unroll
         for (int n = 0; n < C::FN; ++n)
-            acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+
+    // MFMA operands are double-buffered in registers: the LDS reads of
+    // reduction step kk+1 are issued before the MFMAs of step kk, so their
+    // latency hides behind matrix-core work even with one wave per SIMD.
+    bf16x8 af[2][C::FM], bfr[2][C::FN];
+#define COLI_LFRAG(stage_, kk_, slot_)                                                         \
+    do {                                                                                       \
+        const uint16_t *sa_ = lds + (stage_) * C::STAGE;                                       \
+        const uint16_t *sb_ = sa_ + C::BM * C::BK;                                             \
+        const int ch_ = (kk_) * 2 + (lane >> 5);                                               \
+        _Pragma("unroll") for (int m_ = 0; m_ < C::FM; ++m_) af[slot_][m_] =                   \
+            *reinterpret_cast<const bf16x8 *>(sa_ + swz((wm * C::FM + m_) * 32 + (lane & 31), ch_)); \
+        _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_) bfr[slot_][n_] =                  \
+            *reinterpret_cast<const bf16x8 *>(sb_ + swz((wn * C::FN + n_) * 32 + (lane & 31), ch_)); \
+    } while (0)
 
     const int nk = K / C::BK;
     COLI_GLOAD(0);
     COLI_SSTORE(0);
     __syncthreads();
+    COLI_LFRAG(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
         if (kt + 1 < nk) COLI_GLOAD(kt + 1);
-        const uint16_t *sa = lds + (kt & 1) * C::STAGE;
-        const uint16_t *sb = sa + C::BM * C::BK;
 #pragma unroll
-        for (int kk = 0; kk < C::BK / 32; ++kk) {
-            bf16x8 af[C::FM], bfr[C::FN];
-            const int ch = kk * 4 + (lane >> 4);
-#pragma unroll
-            for (int m = 0; m < C::FM; ++m) {
-                int row = (wm * C::FM + m) * 16 + (lane & 15);
-                af[m] = *reinterpret_cast<const bf16x8 *>(sa + swz(row, ch));
-            }
-#pragma unroll
-            for (int n = 0; n < C::FN; ++n) {
-                int row = (wn * C::FN + n) * 16 + (lane & 15);
-                bfr[n] = *reinterpret_cast<const bf16x8 *>(sb + swz(row, ch));
-            }
+        for (int kk = 0; kk < C::BK / 16; ++kk) {
+            const int slot = kk & 1;
+            if (kk + 1 < C::BK / 16) COLI_LFRAG(cur, kk + 1, slot ^ 1);
 #pragma unroll
             for (int m = 0; m < C::FM; ++m)
 #pragma unroll
                 for (int n = 0; n < C::FN; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bfr[n], acc[m][n],
-                                                                        0, 0, 0);
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][m], bfr[slot][n],
+                                                                        acc[m][n], 0, 0, 0);
         }
-        if (kt + 1 < nk) COLI_SSTORE((kt + 1) & 1);
-        __syncthreads();
+        if (kt + 1 < nk) {
+            COLI_SSTORE(cur ^ 1);
+            __syncthreads();
+            COLI_LFRAG(cur ^ 1, 0, 0);
+        }
     }
 #undef COLI_GLOAD
 #undef COLI_SSTORE
+#undef COLI_LFRAG
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS tile engine (large tiles)
+//
+// Same contract as mfma_mainloop, but the tiles travel from global memory
+// straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at
+// M0 + 16 * lane), so no VGPRs are spent on staging and NS stages of BK = 32
+// can be in flight at once (a ring of NS LDS buffers).  A stage holds the
+// BM A rows followed by the BN B rows, 64 bytes (4 chunks) per row; chunk c
+// of row r sits at position c ^ ((r >> 2) & 3), which makes both the 1 KB
+// DMA writes and the 16-rows-per-cycle fragment reads bank-conflict free.
+// Load instruction j of wave w covers rows 16 (4 j + w) .. +15.
+//
+// `valid` = number of real A rows in the tile (1..BM).  A load instruction
+// whose 16 rows are all past `valid` is skipped, and so are the MFMAs and
+// LDS reads of a 32-row fragment past `valid`: a tile of a lightly loaded
+// expert costs little more than streaming its weight rows.  The per-wave
+// count of issued loads is uniform, so the vmcnt waits below stay exact.
+//
+// Per stage kt (frags of reduction step 0 already in registers):
+//   read frags of step 1 | MFMAs of step 0 |
+//   wait for stage kt+1 (own loads), barrier (everyone's loads landed and
+//   everyone left stage kt-1), issue stage kt+NS-1 into kt-1's buffer,
+//   read frags of stage kt+1 step 0 | MFMAs of step 1
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NS_>
+struct DmaCfg {
+    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NS = NS_;
+    static constexpr int BK = 32;
+    static constexpr int FM = BM / (WAVES_M * 32);
+    static constexpr int FN = BN / (WAVES_N * 32);
+    static constexpr int ROWS = BM + BN;
+    static constexpr int LPW = ROWS / 64;               // load instructions per wave per stage
+    static constexpr int STAGE_BYTES = ROWS * 64;
+    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+    static_assert(ROWS % 64 == 0 && BM % 16 == 0, "rows per stage");
+    static_assert(NS >= 3 && (NS & (NS - 1)) == 0, "stages");
+    static_assert(WAVES_M * WAVES_N == 4, "four waves");
+    static_assert(FM >= 1 && FN >= 1, "tile shape");
+};
+
+// Tile row covered by this lane in load instruction j, and the source chunk
+// it must fetch so that the DMA's lane-contiguous layout is the swizzled one.
+template <class C>
+__device__ __forceinline__ int dma_row(int j)
+{
+    return (j * 4 + (threadIdx.x >> 6)) * 16 + ((threadIdx.x & 63) >> 2);
+}
+__device__ __forceinline__ int dma_chunk(int row) { return (threadIdx.x & 3) ^ ((row >> 2) & 3); }
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt unconstrained (gfx9 encoding: vmcnt
+// in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).  n <= 47.
+__device__ __forceinline__ void wait_vmcnt(int n)
+{
+#define COLI_W(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
+    switch (n) {
+        COLI_W(0) COLI_W(1) COLI_W(2) COLI_W(3) COLI_W(4) COLI_W(5) COLI_W(6) COLI_W(7)
+        COLI_W(8) COLI_W(9) COLI_W(10) COLI_W(11) COLI_W(12) COLI_W(13) COLI_W(14) COLI_W(15)
+        COLI_W(16) COLI_W(17) COLI_W(18) COLI_W(19) COLI_W(20) COLI_W(21) COLI_W(22) COLI_W(23)
+        COLI_W(24) COLI_W(25) COLI_W(26) COLI_W(27) COLI_W(28) COLI_W(29) COLI_W(30) COLI_W(31)
+        COLI_W(32) COLI_W(33) COLI_W(34) COLI_W(35) COLI_W(36) COLI_W(37) COLI_W(38) COLI_W(39)
+        COLI_W(40) COLI_W(41) COLI_W(42) COLI_W(43) COLI_W(44) COLI_W(45) COLI_W(46) COLI_W(47)
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+#undef COLI_W
+}
+
+// rp[j]: this lane's source for load instruction j (its row, already offset
+// by dma_chunk), a valid readable address even for padding rows.
+template <class C>
+__device__ __forceinline__ void dma_mainloop(const uint16_t *const (&rp)[C::LPW], int K, int valid,
+                                             char *lds, f32x16 (&acc)[C::FM][C::FN])
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int nk = K / C::BK;
+
+    // load instructions this wave issues per stage (A instructions past
+    // `valid` are skipped; B instructions always run)
+    int nload = 0;
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) {
+        const int q = j * 4 + wave;
+        nload += (q * 16 >= C::BM || q * 16 < valid) ? 1 : 0;
+    }
+
+#define COLI_ISSUE(kt_)                                                                          \
+    do {                                                                                         \
+        char *sb_ = lds + ((kt_) & (C::NS - 1)) * C::STAGE_BYTES;                               \
+        _Pragma("unroll") for (int j_ = 0; j_ < C::LPW; ++j_) {                                 \
+            const int q_ = j_ * 4 + wave;                                                        \
+            if (q_ * 16 >= C::BM || q_ * 16 < valid)                                            \
+                __builtin_amdgcn_global_load_lds(                                                \
+                    (const __attribute__((address_space(1))) void *)(rp[j_] + (kt_) * C::BK),  \
+                    (__attribute__((address_space(3))) void *)(sb_ + q_ * 1024), 16, 0, 0);     \
+        }                                                                                        \
+    } while (0)
+
+    bf16x8 af[2][C::FM], bfr[2][C::FN];
+#define COLI_LFRAG(kt_, kk_, slot_)                                                              \
+    do {                                                                                         \
+        const char *sa_ = lds + ((kt_) & (C::NS - 1)) * C::STAGE_BYTES;                         \
+        const char *sbb_ = sa_ + C::BM * 64;                                                     \
+        const int c_ = (kk_) * 2 + (lane >> 5);                                                 \
+        _Pragma("unroll") for (int m_ = 0; m_ < C::FM; ++m_) {                                  \
+            const int r_ = (wm * C::FM + m_) * 32 + (lane & 31);                                \
+            if ((wm * C::FM + m_) * 32 < valid)                                                  \
+                af[slot_][m_] = *reinterpret_cast<const bf16x8 *>(                               \
+                    sa_ + r_ * 64 + ((c_ ^ ((r_ >> 2) & 3)) << 4));                              \
+        }                                                                                        \
+        _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_) {                                  \
+            const int r_ = (wn * C::FN + n_) * 32 + (lane & 31);                                \
+            bfr[slot_][n_] = *reinterpret_cast<const bf16x8 *>(                                  \
+                sbb_ + r_ * 64 + ((c_ ^ ((r_ >> 2) & 3)) << 4));                                 \
+        }                                                                                        \
+    } while (0)
+#define COLI_MMA(slot_)                                                                          \
+    do {                                                                                         \
+        _Pragma("unroll") for (int m_ = 0; m_ < C::FM; ++m_)                                    \
+            if ((wm * C::FM + m_) * 32 < valid)                                                  \
+                _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_)                            \
+                    acc[m_][n_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                       \
+                        af[slot_][m_], bfr[slot_][n_], acc[m_][n_], 0, 0, 0);                    \
+    } while (0)
+
+#pragma unroll
+    for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+        for (int n = 0; n < C::FN; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+#pragma unroll
+    for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[0][m][i] = af[1][m][i] = (__bf16)0.f;
+
+    // prologue: stages 0 .. NS-2 in flight; wait for stage 0
+#pragma unroll
+    for (int st = 0; st < C::NS - 1; ++st)
+        if (st < nk) COLI_ISSUE(st);
+    wait_vmcnt(min(C::NS - 2, nk - 1) * nload);
+    __syncthreads();
+    COLI_LFRAG(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        COLI_LFRAG(kt, 1, 1);
+        COLI_MMA(0);
+        if (kt + 1 < nk) {
+            wait_vmcnt((min(kt + C::NS - 2, nk - 1) - (kt + 1)) * nload);
+            __syncthreads();
+            if (kt + C::NS - 1 < nk) COLI_ISSUE(kt + C::NS - 1);
+            COLI_LFRAG(kt + 1, 0, 0);
+        }
+        COLI_MMA(1);
+    }
+    // leave LDS quiescent for the caller's epilogue
+    __syncthreads();
+#undef COLI_ISSUE
+#undef COLI_LFRAG
+#undef COLI_MMA
 }
 
 }  // namespace coli

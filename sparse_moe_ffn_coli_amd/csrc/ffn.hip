@@ -24,15 +24,39 @@
 namespace coli {
 
 // ---------------------------------------------------------------------------
-// tile list: for every expert with rows, ceil(count/BM) tiles (expert, m0);
-// then the shared expert's tiles (E, m0) over all T tokens.
-// n_tiles[0] = routed tiles, n_tiles[1] = routed + shared tiles.
+// Work lists.  Every expert with rows is cut into ceil(count/BM) row tiles
+// and, per GEMM, into n_nt column tiles; one entry {expert, first row,
+// column tile} per workgroup.  Within an expert the row tiles are taken in
+// blocks of ROW_BLOCK, and a block's entries are ordered column-tile major,
+// row-tile minor: a block (ROW_BLOCK x n_nt entries) is dispatched together
+// behind one L2 (see xcd_tile), so each weight tile is streamed once per
+// block and shared by its row tiles, and each block of token rows is
+// fetched once and shared by all column tiles.  The gate+up list ends with
+// the shared expert (expert index E over all T tokens); the down list holds
+// the routed experts only.
+// n_items[0] = entries of the down list, n_items[1] = entries of the gate+up list.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
-                                                         int BM, int2 *__restrict__ tiles,
-                                                         int32_t *__restrict__ n_tiles)
+constexpr int ROW_BLOCK = 8;
+
+// Entry `local` of an expert with `mte` row tiles and `nnt` column tiles ->
+// (row tile, column tile) in the block order described above.
+__device__ __forceinline__ int2 block_order(int local, int mte, int nnt)
 {
-    __shared__ int32_t sc[1024];
+    const int per_block = ROW_BLOCK * nnt;
+    const int blk = local / per_block, in = local % per_block;
+    const int rows = min(ROW_BLOCK, mte - blk * ROW_BLOCK);   // the last block may be short
+    return make_int2(blk * ROW_BLOCK + in % rows, in / rows);
+}
+
+__global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
+                                                         int BM, int nnt_gu, int nnt_dn,
+                                                         int4 *__restrict__ list_gu,
+                                                         int4 *__restrict__ list_dn,
+                                                         int32_t *__restrict__ n_items)
+{
+    // sc[e] = row tiles of experts 0..e (inclusive scan); expert E (the
+    // shared one) has ceil(T/BM) row tiles and exists only in the gate+up list
+    __shared__ int32_t sc[1025];
     const int tid = threadIdx.x;
     const int mt = (tid < E) ? (count[tid] + BM - 1) / BM : 0;
     sc[tid] = mt;
@@ -43,46 +67,111 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
         sc[tid] += v;
         __syncthreads();
     }
-    const int start = sc[tid] - mt;
-    for (int i = 0; i < mt; ++i) tiles[start + i] = make_int2(tid, i * BM);
     const int routed = sc[1023];
-    const int n_sh = (T + BM - 1) / BM;
-    for (int i = tid; i < n_sh; i += 1024) tiles[routed + i] = make_int2(E, i * BM);
+    const int mt_sh = (T + BM - 1) / BM;
+    if (tid == 0) sc[1024] = routed + mt_sh;
+    __syncthreads();
+    // expert owning row tile index i: the first e with sc[e] > i
+    auto owner = [&](int i, int last) {
+        int lo = 0, hi = last;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sc[mid] > i) hi = mid; else lo = mid + 1;
+        }
+        return lo;
+    };
+    const int n_gu = (routed + mt_sh) * nnt_gu, n_dn = routed * nnt_dn;
+    // entry index q -> (expert, column tile, row tile), column-major inside an expert
+    for (int q = tid; q < n_gu; q += 1024) {
+        const int e = (q < routed * nnt_gu) ? owner(q / nnt_gu, E - 1) : E;
+        const int mte = (e == E) ? mt_sh : (count[e] + BM - 1) / BM;
+        const int first = (e == E) ? routed : sc[e] - mte;
+        const int2 mn = block_order(q - first * nnt_gu, mte, nnt_gu);
+        list_gu[q] = make_int4(e, mn.x * BM, mn.y, 0);
+    }
+    for (int q = tid; q < n_dn; q += 1024) {
+        const int e = owner(q / nnt_dn, E - 1);
+        const int mte = (count[e] + BM - 1) / BM;
+        const int first = sc[e] - mte;
+        const int2 mn = block_order(q - first * nnt_dn, mte, nnt_dn);
+        list_dn[q] = make_int4(e, mn.x * BM, mn.y, 0);
+    }
     if (tid == 0) {
-        n_tiles[0] = routed;
-        n_tiles[1] = routed + n_sh;
+        n_items[0] = n_dn;
+        n_items[1] = n_gu;
     }
 }
 
 // ---------------------------------------------------------------------------
-// 1. gate+up grouped GEMM with the clamped SwiGLU epilogue.
-// The B tile's BN rows interleave gate and up rows in blocks of 16:
-// block b holds rows f0 + (b >> 1)*16 .. +15 of gate (b even) or up (b odd),
-// so a wave's fragment pair (2j, 2j+1) holds gate and up of the same columns.
+// Tile decode shared by the grouped kernels
+// ---------------------------------------------------------------------------
+struct ExpertTile {
+    int e, m0, cnt, base;   // expert, first row, rows of the expert, first row in h/o
+    bool shared;
+};
+
+__device__ __forceinline__ ExpertTile decode_tile(const int4 &tl, const int32_t *count,
+                                                  const int32_t *offset, int E, int T, int R)
+{
+    ExpertTile r;
+    r.e = tl.x;
+    r.m0 = tl.y;
+    r.shared = (tl.x == E);
+    r.cnt = r.shared ? T : count[tl.x];
+    r.base = r.shared ? R : offset[tl.x];
+    return r;
+}
+
+// Gate/up B rows are interleaved in blocks of 32: block b of a 2*FC-row tile
+// holds rows f0 + (b >> 1) * 32 .. +31 of gate (b even) or up (b odd), so a
+// wave's fragment pair (2j, 2j+1) holds gate and up of the same columns.
+// Rows past F (a ragged last tile) reread row F-1; their outputs are dropped.
+__device__ __forceinline__ const uint16_t *gateup_b_row(const uint16_t *G, const uint16_t *U, int f0,
+                                                        int b, int D, int F)
+{
+    const int blk = b >> 5;
+    const int f = min(f0 + (blk >> 1) * 32 + (b & 31), F - 1);
+    return ((blk & 1) ? U : G) + (size_t)f * D;
+}
+
+// XCD-aware block -> tile map.  Workgroups are dispatched to the 8 XCDs
+// round-robin (block b runs on XCD b % 8).  The actual tile count (known only
+// on the device) is split into 8 contiguous ranges, and the blocks of XCD x
+// take the tiles of range x in order, so tiles that share A rows (same rows,
+// neighbouring columns) or B rows (same expert and columns, neighbouring
+// rows) run at the same time behind the same L2.  The grid is an upper bound;
+// surplus blocks return -1.
+__device__ __forceinline__ int xcd_tile(int ntiles)
+{
+    const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
+    const int per = (ntiles + 7) >> 3;
+    const int t = x * per + w;
+    return (w < per && t < ntiles) ? t : -1;
+}
+
+// ---------------------------------------------------------------------------
+// 1. gate+up grouped GEMM with the clamped SwiGLU in the epilogue, h in bf16.
 // ---------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(256) void gateup_bf16_kernel(
+__global__ __launch_bounds__(256) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, const int2 *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
+    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
     int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
 {
     static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    constexpr int FCOLS = C::BN / 2;
-    const int n_nt = F / FCOLS;
-    const int ti = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
-    if (ti >= n_tiles[1]) return;
-    const int2 tile = tiles[ti];
-    const int e = tile.x, m0 = tile.y;
-    const bool shared = (e == E);
+    constexpr int FC = C::BN / 2;                 // output columns per tile
+    const int t = xcd_tile(n_items[1]);
+    if (t < 0) return;
+    const int4 item = list[t];
+    const int nt = item.z;
     const int R = T * K;
-    const int cnt = shared ? T : count[e];
-    const int hbase = shared ? R : offset[e];
-    const uint16_t *G = shared ? s_gate : gate + (size_t)e * F * D;
-    const uint16_t *U = shared ? s_up : up + (size_t)e * F * D;
-    const int f0 = nt * FCOLS;
+    const ExpertTile et = decode_tile(item, count, offset, E, T, R);
+    const uint16_t *G = et.shared ? s_gate : gate + (size_t)et.e * F * D;
+    const uint16_t *U = et.shared ? s_up : up + (size_t)et.e * F * D;
+    const int f0 = nt * FC;
     const int ch0 = threadIdx.x & 7;
 
     const uint16_t *ap[C::A_PER_T];
@@ -90,19 +179,14 @@ __global__ __launch_bounds__(256) void gateup_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i) {
         // padding rows (past the expert's last row) reread its first row
-        int r = m0 + a_chunk_row<C>(i);
-        if (a_chunk_row<C>(i) >= C::BM || r >= cnt) r = m0;
-        const int t = shared ? r : perm[hbase + r] / K;
-        ap[i] = x + (size_t)t * D + ch0 * 8;
+        int r = et.m0 + a_chunk_row<C>(i);
+        if (a_chunk_row<C>(i) >= C::BM || r >= et.cnt) r = et.m0;
+        const int tok = et.shared ? r : perm[et.base + r] / K;
+        ap[i] = x + (size_t)tok * D + ch0 * 8;
     }
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-        int rr = a_chunk_row<C>(i);
-        int blk = rr >> 4;
-        int f = f0 + (blk >> 1) * 16 + (rr & 15);
-        bp[i] = ((blk & 1) ? U : G) + (size_t)f * D + ch0 * 8;
-    }
-    f32x4 acc[C::FM][C::FN];
+    for (int i = 0; i < C::B_PER_T; ++i) bp[i] = gateup_b_row(G, U, f0, a_chunk_row<C>(i), D, F) + ch0 * 8;
+    f32x16 acc[C::FM][C::FN];
     mfma_mainloop<C>(ap, bp, D, lds, acc);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -111,33 +195,32 @@ __global__ __launch_bounds__(256) void gateup_bf16_kernel(
     for (int m = 0; m < C::FM; ++m)
 #pragma unroll
         for (int n = 0; n < C::FN; n += 2) {
-            const int f = f0 + ((wn * C::FN + n) >> 1) * 16 + (lane & 15);
+            const int f = f0 + ((wn * C::FN + n) >> 1) * 32 + (lane & 31);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int r = m0 + (wm * C::FM + m) * 16 + 4 * (lane >> 4) + i;
-                if (r < cnt)
-                    h[(size_t)(hbase + r) * F + f] =
+            for (int i = 0; i < 16; ++i) {
+                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
+                if (r < et.cnt && f < F)
+                    h[(size_t)(et.base + r) * F + f] =
                         f32_to_bf16_bits(swiglu_clamped(acc[m][n][i], acc[m][n + 1][i]));
             }
         }
 }
 
 // ---------------------------------------------------------------------------
-// 2. down grouped GEMM over the routed rows: o[row] = W_down[e] h[row].
+// 2. down grouped GEMM over the routed rows: o[row] = W_down[e] h[row], o in bf16.
 // ---------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(256) void down_bf16_kernel(
+__global__ __launch_bounds__(256) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ down,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int2 *__restrict__ tiles, const int32_t *__restrict__ n_tiles, int D, int F,
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int F,
     uint16_t *__restrict__ o)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const int n_nt = (D + C::BN - 1) / C::BN;      // the last n-tile may be ragged
-    const int ti = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
-    if (ti >= n_tiles[0]) return;
-    const int2 tile = tiles[ti];
-    const int e = tile.x, m0 = tile.y;
+    const int t = xcd_tile(n_items[0]);
+    if (t < 0) return;
+    const int4 item = list[t];
+    const int e = item.x, m0 = item.y, nt = item.z;   // the last column tile may be ragged
     const int cnt = count[e];
     const int base = offset[e];
     const int d0 = nt * C::BN;
@@ -156,7 +239,7 @@ __global__ __launch_bounds__(256) void down_bf16_kernel(
         int d = min(d0 + a_chunk_row<C>(i), D - 1);    // rows past D reread the last one
         bp[i] = down + ((size_t)e * D + d) * F + ch0 * 8;
     }
-    f32x4 acc[C::FM][C::FN];
+    f32x16 acc[C::FM][C::FN];
     mfma_mainloop<C>(ap, bp, F, lds, acc);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -165,10 +248,10 @@ __global__ __launch_bounds__(256) void down_bf16_kernel(
     for (int m = 0; m < C::FM; ++m)
 #pragma unroll
         for (int n = 0; n < C::FN; ++n) {
-            const int d = d0 + (wn * C::FN + n) * 16 + (lane & 15);
+            const int d = d0 + acc_col<C>(wn, n, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int r = m0 + (wm * C::FM + m) * 16 + 4 * (lane >> 4) + i;
+            for (int i = 0; i < 16; ++i) {
+                const int r = m0 + acc_row<C>(wm, m, lane, i);
                 if (r < cnt && d < D) o[(size_t)(base + r) * D + d] = f32_to_bf16_bits(acc[m][n][i]);
             }
         }
@@ -178,6 +261,9 @@ __global__ __launch_bounds__(256) void down_bf16_kernel(
 // 3. shared down GEMM over the tokens with the combine in the epilogue:
 //    v = S(x_t)[d]; v = fmaf(w_tj, o[inv(t,j)][d], v) for j = 0..K-1;
 //    y = residual + v.
+// The GEMM result is staged through LDS so that each thread then owns 8
+// consecutive columns of one token and reads the routed rows of o with
+// 16-byte loads.
 // ---------------------------------------------------------------------------
 template <class C>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
@@ -185,6 +271,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const float *__restrict__ w, const int32_t *__restrict__ inv, const float *residual, int T, int D,
     int K, int F, float *y, uint16_t *__restrict__ y_bf16)
 {
+    static_assert(C::BM * C::BN * 4 <= C::LDS_BYTES, "epilogue staging fits the tile's LDS");
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
     const int n_nt = (D + C::BN - 1) / C::BN;
     const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
@@ -205,39 +292,70 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
         int d = min(d0 + a_chunk_row<C>(i), D - 1);
         bp[i] = s_down + (size_t)d * F + ch0 * 8;
     }
-    f32x4 acc[C::FM][C::FN];
+    f32x16 acc[C::FM][C::FN];
     mfma_mainloop<C>(ap, bp, F, lds, acc);
 
+    // stage S(x) for the tile: sx[row][col] fp32, once every wave is done
+    // reading the mainloop's last stage
+    __syncthreads();
+    float *sx = reinterpret_cast<float *>(lds);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
 #pragma unroll
     for (int m = 0; m < C::FM; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + (wm * C::FM + m) * 16 + 4 * (lane >> 4) + i;
-            if (t >= T) continue;
-            int rows[8];
-            float wt[8];
+        for (int n = 0; n < C::FN; ++n) {
+            const int c = acc_col<C>(wn, n, lane);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j < K) {
-                    rows[j] = inv[(size_t)t * K + j];
-                    wt[j] = w[(size_t)t * K + j];
+            for (int i = 0; i < 16; ++i) sx[acc_row<C>(wm, m, lane, i) * C::BN + c] = acc[m][n][i];
+        }
+    __syncthreads();
+
+    constexpr int CHUNKS = C::BM * C::BN / 8;
+    for (int q = threadIdx.x; q < CHUNKS; q += C::NT) {
+        const int row = q / (C::BN / 8), c8 = (q % (C::BN / 8)) * 8;
+        const int t = t0 + row, d = d0 + c8;
+        if (t >= T || d >= D) continue;
+        // all routed rows of the token are fetched before the fixed-order sum
+        float wj[8];
+        u32x4 ov[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K) {
+                wj[j] = w[(size_t)t * K + j];
+                ov[j] = *reinterpret_cast<const u32x4 *>(o + (size_t)inv[(size_t)t * K + j] * D + d);
+            }
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = sx[row * C::BN + c8 + k];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    v[2 * k] = fmaf(wj[j], __uint_as_float(ov[j][k] << 16), v[2 * k]);
+                    v[2 * k + 1] = fmaf(wj[j], __uint_as_float(ov[j][k] & 0xffff0000u), v[2 * k + 1]);
                 }
+        const size_t idx = (size_t)t * D + d;
+        if (residual) {
+            const f32x4 r0 = *reinterpret_cast<const f32x4 *>(residual + idx);
+            const f32x4 r1 = *reinterpret_cast<const f32x4 *>(residual + idx + 4);
 #pragma unroll
-            for (int n = 0; n < C::FN; ++n) {
-                const int d = d0 + (wn * C::FN + n) * 16 + (lane & 15);
-                if (d >= D) continue;
-                float v = acc[m][n][i];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (j < K) v = fmaf(wt[j], bf16_bits_to_f32(o[(size_t)rows[j] * D + d]), v);
-                const size_t idx = (size_t)t * D + d;
-                if (residual) v = residual[idx] + v;
-                y[idx] = v;
-                if (y_bf16) y_bf16[idx] = f32_to_bf16_bits(v);
+            for (int k = 0; k < 4; ++k) {
+                v[k] = r0[k] + v[k];
+                v[4 + k] = r1[k] + v[4 + k];
             }
         }
+        *reinterpret_cast<f32x4 *>(y + idx) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4 *>(y + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        if (y_bf16) {
+            u32x4 pk;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                pk[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
+            *reinterpret_cast<u32x4 *>(y_bf16 + idx) = pk;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -309,14 +427,16 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-using Cfg16 = TileCfg<16, 128, 1, 4>;
-using Cfg128 = TileCfg<128, 128, 2, 2>;
+using SmallCfg = TileCfg<32, 256, 1, 4>;
+using LargeCfg = TileCfg<64, 256, 2, 2>;
+using CombineCfg = TileCfg<64, 128, 2, 2>;
+static_assert(SmallCfg::BN == LargeCfg::BN, "both paths cut columns alike");
 
 int ffn_tile_rows(int T, int E, int K)
 {
     // rows per expert on average decides the tile height
     const long R = (long)T * K;
-    return (R <= 24L * E) ? 16 : 128;
+    return (R <= 24L * E) ? SmallCfg::BM : LargeCfg::BM;
 }
 
 long ffn_max_tiles(int T, int E, int K, int bm)
@@ -325,27 +445,38 @@ long ffn_max_tiles(int T, int E, int K, int bm)
     return R / bm + (R < E ? R : E) + (T + bm - 1) / bm;
 }
 
-template <class C>
-static void launch_bf16_gemms(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
+int ffn_col_tiles_gu(int F) { return (F + LargeCfg::BN / 2 - 1) / (LargeCfg::BN / 2); }
+int ffn_col_tiles_dn(int D) { return (D + LargeCfg::BN - 1) / LargeCfg::BN; }
+
+static void launch_combine(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
-    const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
-    const uint16_t *h = (const uint16_t *)a.h;
-    mk.mark(st);
-    gateup_bf16_kernel<C><<<(unsigned)(mt * (a.F / (C::BN / 2))), 256, 0, st>>>(
-        (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
-        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.tiles,
-        a.n_tiles, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+    using C = CombineCfg;
     const int n_nt_d = (a.D + C::BN - 1) / C::BN;
-    mk.mark(st);
-    down_bf16_kernel<C><<<(unsigned)(mt * n_nt_d), 256, 0, st>>>(
-        h, (const uint16_t *)a.down, a.count, a.offset, a.tiles, a.n_tiles, a.D, a.F,
-        (uint16_t *)a.o);
     const int n_mt = (a.T + C::BM - 1) / C::BM;
     mk.mark(st);
     combine_bf16_kernel<C><<<(unsigned)(n_mt * n_nt_d), 256, 0, st>>>(
-        h, (const uint16_t *)a.s_down, (const uint16_t *)a.o, a.w, a.inv, a.residual, a.T, a.D, a.K,
-        a.F, a.y, (uint16_t *)a.y_bf16);
+        (const uint16_t *)a.h, (const uint16_t *)a.s_down, (const uint16_t *)a.o, a.w, a.inv,
+        a.residual, a.T, a.D, a.K, a.F, a.y, (uint16_t *)a.y_bf16);
     mk.mark(st);
+}
+
+template <class C>
+static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
+{
+    // grids are upper bounds of the list lengths (rounded to whole XCD groups)
+    const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
+    const long grid_gu = ((mt * ffn_col_tiles_gu(a.F) + 7) / 8) * 8;
+    const long grid_dn = ((mt * ffn_col_tiles_dn(a.D) + 7) / 8) * 8;
+    mk.mark(st);
+    gateup_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
+        (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.list_gu,
+        a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+    mk.mark(st);
+    down_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
+        (const uint16_t *)a.h, (const uint16_t *)a.down, a.count, a.offset, a.list_dn, a.n_items, a.D,
+        a.F, (uint16_t *)a.o);
+    launch_combine(a, mk, st);
 }
 
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
@@ -356,11 +487,12 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
     StageMarks &mk = a.marks ? *a.marks : none;
     mk.mark(st);
     if (a.bf16) {
-        ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, T, a.bm, a.tiles, a.n_tiles);
-        if (a.bm == 16)
-            launch_bf16_gemms<Cfg16>(a, mk, st);
+        ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, T, a.bm, ffn_col_tiles_gu(F),
+                                             ffn_col_tiles_dn(D), a.list_gu, a.list_dn, a.n_items);
+        if (a.bm == SmallCfg::BM)
+            launch_staged<SmallCfg>(a, mk, st);
         else
-            launch_bf16_gemms<Cfg128>(a, mk, st);
+            launch_staged<LargeCfg>(a, mk, st);
     } else {
         const int64_t n1 = (int64_t)(R + T) * F, n2 = (int64_t)R * D, n3 = (int64_t)T * D;
         mk.mark(st);

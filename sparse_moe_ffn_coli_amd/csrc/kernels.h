@@ -26,8 +26,8 @@ struct RouteLaunch {
     const void *wr;
     const float *bias;
     float *z;              // workspace [T][E]
-    int32_t *tile_count;   // workspace [ceil(T/64)][E]
-    int32_t *tile_base;    // workspace [ceil(T/64)][E]
+    int32_t *tile_count;   // workspace [perm_tiles(T)][E]
+    int32_t *tile_base;    // workspace [perm_tiles(T)][E]
     int32_t *ids;
     float *w;
     int32_t *count, *offset, *perm, *inv;
@@ -48,15 +48,19 @@ struct FfnLaunch {
     void *y_bf16;
     void *h;               // workspace [T*K + T][F]
     void *o;               // workspace [T*K][D]
-    int2 *tiles;           // workspace [ffn_max_tiles]
-    int32_t *n_tiles;      // workspace [2]
+    int4 *list_gu;         // workspace [ffn_max_tiles * ffn_col_tiles_gu]
+    int4 *list_dn;         // workspace [ffn_max_tiles * ffn_col_tiles_dn]
+    int32_t *n_items;      // workspace [2]
     StageMarks *marks;     // nullable
 };
 
 hipError_t launch_route(const RouteLaunch &a, hipStream_t st);
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st);
 
+int perm_tiles(int T);
 int ffn_tile_rows(int T, int E, int K);
 long ffn_max_tiles(int T, int E, int K, int bm);
+int ffn_col_tiles_gu(int F);
+int ffn_col_tiles_dn(int D);
 
 }  // namespace coli

@@ -19,50 +19,76 @@
 namespace coli {
 
 // ---------------------------------------------------------------------------
-// router logits, bf16 inputs, MFMA.  One workgroup per (16-token block,
-// 128-expert block); rows past T and experts past E are zero-padded.
+// router logits, bf16 inputs, MFMA.  One workgroup per (32-token block,
+// 32*NF-expert block); the four waves split the reduction dimension into
+// quarters and stream their operands straight from global memory into MFMA
+// registers (each wave's data is its own, so no LDS staging).  The four
+// partial 32x64 blocks are added in LDS in wave order -- a fixed order, so
+// the logits are bitwise reproducible -- and the bias is added last.  Rows
+// past T and experts past E reread a valid row; their results are dropped.
 // ---------------------------------------------------------------------------
-using RouterCfg = TileCfg<16, 128, 1, 4>;
+constexpr int RT_M = 32;
+constexpr int RT_BATCH = 8;         // reduction steps whose operands are loaded ahead
 
+template <int NF>                    // 32-expert fragments per workgroup
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, const float *__restrict__ bias,
     int T, int D, int E, float *__restrict__ z)
 {
-    using C = RouterCfg;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const int n_nt = (E + C::BN - 1) / C::BN;
+    __shared__ float red[4 * NF * 16 * 64];         // [wave][frag][i][lane]
+    const int n_nt = (E + 32 * NF - 1) / (32 * NF);
     const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
-    const int t0 = mt * C::BM, e0 = nt * C::BN;
-    const int ch0 = threadIdx.x & 7;
-
-    const uint16_t *ap[C::A_PER_T];
-    const uint16_t *bp[C::B_PER_T];
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-        int t = min(t0 + a_chunk_row<C>(i), T - 1);      // padding rows reread the last token
-        ap[i] = x + (size_t)t * D + ch0 * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-        int e = min(e0 + a_chunk_row<C>(i), E - 1);      // padding rows reread the last expert
-        bp[i] = wr + (size_t)e * D + ch0 * 8;
-    }
-    f32x4 acc[C::FM][C::FN];
-    mfma_mainloop<C>(ap, bp, D, lds, acc);
-
+    const int t0 = mt * RT_M, e0 = nt * 32 * NF;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
+    const int kq = D / 4, kbeg = wave * kq + 8 * (lane >> 5);
+    const uint16_t *pa = x + (size_t)min(t0 + (lane & 31), T - 1) * D + kbeg;
+    const uint16_t *pb[NF];
 #pragma unroll
-    for (int m = 0; m < C::FM; ++m)
+    for (int f = 0; f < NF; ++f) pb[f] = wr + (size_t)min(e0 + 32 * f + (lane & 31), E - 1) * D + kbeg;
+    f32x16 acc[NF];
 #pragma unroll
-        for (int n = 0; n < C::FN; ++n) {
-            int e = e0 + (wn * C::FN + n) * 16 + (lane & 15);
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int t = t0 + (wm * C::FM + m) * 16 + 4 * (lane >> 4) + i;
-                if (t < T && e < E) z[(size_t)t * E + e] = acc[m][n][i] + bias[e];
-            }
+        for (int i = 0; i < 16; ++i) acc[f][i] = 0.f;
+    int k = 0;
+    // batches of RT_BATCH steps: all loads of a batch are issued before its MFMAs
+    for (; k + 16 * RT_BATCH <= kq; k += 16 * RT_BATCH) {
+        bf16x8 a[RT_BATCH], b[RT_BATCH][NF];
+#pragma unroll
+        for (int u = 0; u < RT_BATCH; ++u) {
+            a[u] = *reinterpret_cast<const bf16x8 *>(pa + k + 16 * u);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) b[u][f] = *reinterpret_cast<const bf16x8 *>(pb[f] + k + 16 * u);
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep the whole batch of loads ahead of the MFMAs
+#pragma unroll
+        for (int u = 0; u < RT_BATCH; ++u)
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u][f], acc[f], 0, 0, 0);
+    }
+    for (; k < kq; k += 16) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(pa + k);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+            acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, *reinterpret_cast<const bf16x8 *>(pb[f] + k), acc[f], 0, 0, 0);
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[((wave * NF + f) * 16 + i) * 64 + lane] = acc[f][i];
+    __syncthreads();
+    for (int q = threadIdx.x; q < NF * 16 * 64; q += 256) {
+        const int f = q >> 10, i = (q >> 6) & 15, ln = q & 63;
+        float v = red[((0 * NF + f) * 16 + i) * 64 + ln];
+        v += red[((1 * NF + f) * 16 + i) * 64 + ln];
+        v += red[((2 * NF + f) * 16 + i) * 64 + ln];
+        v += red[((3 * NF + f) * 16 + i) * 64 + ln];
+        const int t = t0 + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
+        const int e = e0 + f * 32 + (ln & 31);
+        if (t < T && e < E) z[(size_t)t * E + e] = v + bias[e];
+    }
 }
 
 // fp32 router: one thread per (token, expert), plain dot product.
@@ -80,9 +106,11 @@ __global__ void router_logits_f32_kernel(const float *__restrict__ x, const floa
 }
 
 // ---------------------------------------------------------------------------
-// top-K: one wave per token.  Keys are (order-preserving image of the fp32
-// logit) << 32 | (0xFFFFFFFF - expert), so the largest key is the largest
-// logit with the lowest index on ties; K rounds of a wave-wide max.
+// top-K: one wave per token.  Lane l holds the logits of experts l, l+64, ...
+// as order-preserving unsigned images of the fp32 values.  Each of the K
+// rounds takes the wave-wide maximum value, then, among the lanes holding
+// it, the lowest expert index (ties go to the lower index), and removes that
+// expert.  Both reductions run on DPP lane permutations.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ordered_bits(float f)
 {
@@ -96,19 +124,9 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o)
     return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
 constexpr int TOPK_MAX_E = 1024;
-constexpr int TOPK_SLOTS = TOPK_MAX_E / 64;
 
+template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ z, int T, int E, int K,
                                                    int32_t *__restrict__ ids, float *__restrict__ w)
 {
@@ -117,29 +135,33 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ z, 
     if (t >= T) return;
     const float *zt = z + (size_t)t * E;
 
-    uint64_t key[TOPK_SLOTS];
+    // 0 marks an empty slot; every real logit maps above 0 (NaN aside)
+    uint32_t key[SLOTS];
 #pragma unroll
-    for (int s = 0; s < TOPK_SLOTS; ++s) {
-        int e = lane + 64 * s;
-        key[s] = (e < E) ? ((uint64_t)ordered_bits(zt[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
-                         : 0ull;
+    for (int s = 0; s < SLOTS; ++s) {
+        const int e = lane + 64 * s;
+        key[s] = (e < E) ? ordered_bits(zt[e]) : 0u;
     }
     int sel_e[8];
     float sel_z[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (j >= K) { sel_e[j] = 0x7fffffff; sel_z[j] = 0.f; continue; }
-        uint64_t best = 0;
+        // this lane's best: largest key, lowest slot on ties
+        uint32_t best = key[0];
+        int bslot = 0;
 #pragma unroll
-        for (int s = 0; s < TOPK_SLOTS; ++s) best = key[s] > best ? key[s] : best;
-        best = wave_max_u64(best);
-        int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+        for (int s = 1; s < SLOTS; ++s)
+            if (key[s] > best) { best = key[s]; bslot = s; }
+        const uint32_t m = wave_reduce_u32(best, MaxU32());
+        const uint32_t cand = (best == m) ? (uint32_t)(bslot * 64 + lane) : 0xFFFFFFFFu;
+        const int e = (int)wave_reduce_u32(cand, MinU32());
         sel_e[j] = e;
-        sel_z[j] = from_ordered_bits((uint32_t)(best >> 32));
+        sel_z[j] = from_ordered_bits(m);
         if ((e & 63) == lane) {
 #pragma unroll
-            for (int s = 0; s < TOPK_SLOTS; ++s)
-                if (s == (e >> 6)) key[s] = 0ull;
+            for (int s = 0; s < SLOTS; ++s)
+                if (s == (e >> 6)) key[s] = 0u;
         }
     }
     // canonical order: ascending expert id
@@ -180,29 +202,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ z, 
 }
 
 // ---------------------------------------------------------------------------
-// permutation
+// permutation.  Tiles of 256 tokens, one workgroup of 4 waves each; wave w
+// builds one bitmask per expert over its 64 tokens (bit l = token 64w + l of
+// the tile chose the expert).  A token's rank among the tile's tokens of an
+// expert is the popcount of the earlier waves' masks plus the popcount of its
+// own wave's mask below its lane.
 // ---------------------------------------------------------------------------
-// Bitmask of the tile's tokens (one bit per lane) that chose each expert.
+constexpr int PERM_TILE = 256;
+
 __device__ __forceinline__ void build_tile_masks(const int32_t *__restrict__ ids, int T, int E, int K,
                                                  uint64_t *masks)
 {
-    const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += 64) masks[e] = 0ull;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < 4 * E; i += PERM_TILE) masks[i] = 0ull;
     __syncthreads();
-    const int t = blockIdx.x * 64 + lane;
+    const int t = blockIdx.x * PERM_TILE + threadIdx.x;
     if (t < T)
-        for (int j = 0; j < K; ++j) atomicOr((unsigned long long *)&masks[ids[(size_t)t * K + j]],
-                                             1ull << lane);
+        for (int j = 0; j < K; ++j)
+            atomicOr((unsigned long long *)&masks[wave * E + ids[(size_t)t * K + j]], 1ull << lane);
     __syncthreads();
 }
 
-__global__ __launch_bounds__(64) void perm_hist_kernel(const int32_t *__restrict__ ids, int T, int E,
-                                                       int K, int32_t *__restrict__ tile_count)
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restrict__ ids, int T, int E,
+                                                        int K, int32_t *__restrict__ tile_count)
 {
-    __shared__ uint64_t masks[TOPK_MAX_E];
+    __shared__ uint64_t masks[4 * TOPK_MAX_E];
     build_tile_masks(ids, T, E, K, masks);
-    for (int e = threadIdx.x; e < E; e += 64)
-        tile_count[(size_t)blockIdx.x * E + e] = __popcll(masks[e]);
+    for (int e = threadIdx.x; e < E; e += PERM_TILE)
+        tile_count[(size_t)blockIdx.x * E + e] = __popcll(masks[e]) + __popcll(masks[E + e]) +
+                                                 __popcll(masks[2 * E + e]) + __popcll(masks[3 * E + e]);
 }
 
 // One workgroup: count[e] = sum over tiles; offset = exclusive scan of count;
@@ -239,20 +267,22 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t *__restri
     }
 }
 
-__global__ __launch_bounds__(64) void perm_scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
-                                                          int K, const int32_t *__restrict__ tile_base,
-                                                          int32_t *__restrict__ perm,
-                                                          int32_t *__restrict__ inv)
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
+                                                           int K, const int32_t *__restrict__ tile_base,
+                                                           int32_t *__restrict__ perm,
+                                                           int32_t *__restrict__ inv)
 {
-    __shared__ uint64_t masks[TOPK_MAX_E];
+    __shared__ uint64_t masks[4 * TOPK_MAX_E];
     build_tile_masks(ids, T, E, K, masks);
-    const int lane = threadIdx.x;
-    const int t = blockIdx.x * 64 + lane;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * PERM_TILE + threadIdx.x;
     if (t >= T) return;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int j = 0; j < K; ++j) {
-        int e = ids[(size_t)t * K + j];
-        int row = tile_base[(size_t)blockIdx.x * E + e] + __popcll(masks[e] & below);
+        const int e = ids[(size_t)t * K + j];
+        int rank = __popcll(masks[wave * E + e] & below);
+        for (int w2 = 0; w2 < wave; ++w2) rank += __popcll(masks[w2 * E + e]);
+        const int row = tile_base[(size_t)blockIdx.x * E + e] + rank;
         perm[row] = t * K + j;
         inv[(size_t)t * K + j] = row;
     }
@@ -261,6 +291,8 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(const int32_t *__restr
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+int perm_tiles(int T) { return (T + PERM_TILE - 1) / PERM_TILE; }
+
 // T = 0: no tokens, but count and offset are still defined (all zero).
 __global__ void route_empty_kernel(int E, int32_t *__restrict__ count, int32_t *__restrict__ offset)
 {
@@ -281,24 +313,35 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
     StageMarks &mk = a.marks ? *a.marks : none;
     mk.mark(st);
     if (a.bf16) {
-        int n_nt = (E + RouterCfg::BN - 1) / RouterCfg::BN;
-        int n_mt = (T + RouterCfg::BM - 1) / RouterCfg::BM;
-        router_logits_bf16_kernel<<<n_mt * n_nt, 256, 0, st>>>(
-            (const uint16_t *)a.x, (const uint16_t *)a.wr, a.bias, T, D, E, a.z);
+        // small batches: 32-expert blocks for more workgroups; large: 64
+        const int n_mt = (T + RT_M - 1) / RT_M;
+        if (T <= 512)
+            router_logits_bf16_kernel<1><<<n_mt * ((E + 31) / 32), 256, 0, st>>>(
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.bias, T, D, E, a.z);
+        else
+            router_logits_bf16_kernel<2><<<n_mt * ((E + 63) / 64), 256, 0, st>>>(
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.bias, T, D, E, a.z);
     } else {
         int64_t n = (int64_t)T * E;
         router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
             (const float *)a.x, (const float *)a.wr, a.bias, T, D, E, a.z);
     }
     mk.mark(st);
-    topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
-    const int ntiles = (T + 63) / 64;
+    {
+        const int g = (T + 3) / 4, slots = (E + 63) / 64;
+        if (slots <= 1) topk_kernel<1><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
+        else if (slots <= 2) topk_kernel<2><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
+        else if (slots <= 4) topk_kernel<4><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
+        else if (slots <= 8) topk_kernel<8><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
+        else topk_kernel<16><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
+    }
+    const int ntiles = perm_tiles(T);
     mk.mark(st);
-    perm_hist_kernel<<<ntiles, 64, 0, st>>>(a.ids, T, E, K, a.tile_count);
+    perm_hist_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_count);
     mk.mark(st);
     perm_scan_kernel<<<1, 1024, 0, st>>>(a.tile_count, ntiles, E, a.tile_base, a.count, a.offset);
     mk.mark(st);
-    perm_scatter_kernel<<<ntiles, 64, 0, st>>>(a.ids, T, E, K, a.tile_base, a.perm, a.inv);
+    perm_scatter_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_base, a.perm, a.inv);
     mk.mark(st);
     return hipGetLastError();
 }
