@@ -251,13 +251,44 @@ coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
                                     size_t ws_bytes, void *stream, void *const *events,
                                     int32_t n_events)
 {
-    (void)events; (void)n_events;
-    (void)x; (void)r; (void)residual; (void)y; (void)y_bf16; (void)ws; (void)ws_bytes; (void)stream;
     coli_status st = check_shape(s);
     if (st != COLI_OK) return st;
     if (!w) return COLI_E_NULL;
     if (s->dtype != COLI_BF16) return COLI_E_DTYPE;
-    return COLI_E_SHAPE;   // int4 kernels are not built yet
+    if (w->group <= 0 || w->group % 32 || s->D % w->group || s->F % w->group) return COLI_E_SHAPE;
+    if (s->T == 0) return check_device();
+    if (!w->gate_q || !w->up_q || !w->down_q || !w->gate_s || !w->up_s || !w->down_s || !w->s_gate ||
+        !w->s_up || !w->s_down)
+        return COLI_E_NULL;
+    if (!aligned16(w->gate_q) || !aligned16(w->up_q) || !aligned16(w->down_q) || !aligned16(w->gate_s) ||
+        !aligned16(w->up_s) || !aligned16(w->down_s) || !aligned16(w->s_gate) || !aligned16(w->s_up) ||
+        !aligned16(w->s_down))
+        return COLI_E_ALIGN;
+    const FfnWs L = ffn_ws(s, 1);
+    if ((st = ffn_common_checks(s, x, r, residual, y, y_bf16, ws, ws_bytes, L.total)) != COLI_OK)
+        return st;
+
+    coli::FfnLaunch a{};
+    a.T = s->T; a.D = s->D; a.E = s->E; a.K = s->K; a.F = s->F;
+    a.bf16 = true;
+    a.bm = L.bm;
+    a.x = x;
+    a.ids = r->ids; a.w = r->w; a.count = r->count; a.offset = r->offset; a.perm = r->perm;
+    a.inv = r->inv;
+    a.use_int4 = true;
+    a.gate_q = w->gate_q; a.up_q = w->up_q; a.down_q = w->down_q;
+    a.gate_s = w->gate_s; a.up_s = w->up_s; a.down_s = w->down_s;
+    a.group = w->group;
+    a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
+    a.residual = residual; a.y = y; a.y_bf16 = y_bf16;
+    char *base = (char *)ws;
+    a.h = base + L.h; a.o = base + L.o;
+    a.list_gu = (int4 *)(base + L.list_gu);
+    a.list_dn = (int4 *)(base + L.list_dn);
+    a.n_items = (int32_t *)(base + L.n_items);
+    coli::StageMarks marks{events, n_events, 0};
+    a.marks = &marks;
+    return coli::launch_ffn(a, (hipStream_t)stream) == hipSuccess ? COLI_OK : COLI_E_LAUNCH;
 }
 
 }  // extern "C"

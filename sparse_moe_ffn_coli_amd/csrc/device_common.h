@@ -230,6 +230,156 @@ __device__ __forceinline__ void mfma_mainloop(const uint16_t *const (&ap)[C::A_P
 }
 
 // ---------------------------------------------------------------------------
+// fp16 variant of the register-staged engine, for int4 weights
+//
+// Operands are fp16 in LDS and multiplied with v_mfma_f32_32x32x16_f16 (fp32
+// accumulation).  A rows arrive in bf16 and are converted on the way into
+// LDS (exact for magnitudes in fp16's normal range).  Each of the BN (= 256
+// = threads) B rows is staged by one thread, one of two ways per tile:
+//   int4: 32 bytes of nibbles per K step of 64, element 2i in the low nibble
+//         of byte i, value (nibble - 8) * scale with one fp16 scale per
+//         `group` consecutive elements (offset-binary, "feat(glm53): add
+//         device-resident HIP backend for MI350P", section "Key changes");
+//         the product is formed in fp32 (exact) and rounded once to fp16;
+//   bf16: converted like the A rows (the shared expert's dense weights).
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v)
+{
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const _Float16 lo = (_Float16)__uint_as_float(v[k] << 16);
+        const _Float16 hi = (_Float16)__uint_as_float(v[k] & 0xffff0000u);
+        r[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return r;
+}
+
+// 8 nibbles (elements 0..7 of a chunk; element 2i in the low nibble of byte i)
+// -> 8 fp16 values (nibble - 8) * scale
+__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, float scale)
+{
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float a = (float)((int)((w >> (8 * k)) & 0xF) - 8) * scale;
+        const float b = (float)((int)((w >> (8 * k + 4)) & 0xF) - 8) * scale;
+        r[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    }
+    return r;
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint16_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ap: A rows (bf16) as in mfma_mainloop.  B row of this thread (row tid):
+// int4 when bq != nullptr (nibbles bq, fp16 scales bs, `group` elements per
+// scale, a multiple of 32), else bf16 row bb.
+template <class C>
+__device__ __forceinline__ void mfma_mainloop_f16(const uint16_t *const (&ap)[C::A_PER_T],
+                                                  const uint16_t *bb, const uint8_t *bq,
+                                                  const uint16_t *bs, int group, int K, uint16_t *lds,
+                                                  f32x16 (&acc)[C::FM][C::FN])
+{
+    static_assert(C::BN == C::NT, "one B row per thread");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int ch0 = tid & 7;
+    const bool i4 = bq != nullptr;
+
+    u32x4 ra[C::A_PER_T];
+    u32x4 rq[2];
+    u32x4 rb[8];
+    float s0 = 0.f, s1 = 0.f;
+#define COLI_GLOAD16(kt_)                                                                      \
+    do {                                                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < C::A_PER_T; ++i_) ra[i_] =                     \
+            *reinterpret_cast<const u32x4 *>(ap[i_] + (kt_) * C::BK);                          \
+        if (i4) {                                                                              \
+            rq[0] = *reinterpret_cast<const u32x4 *>(bq + (kt_) * (C::BK / 2));                \
+            rq[1] = *reinterpret_cast<const u32x4 *>(bq + (kt_) * (C::BK / 2) + 16);           \
+            s0 = fp16_bits_to_f32(bs[((kt_) * C::BK) / group]);                               \
+            s1 = fp16_bits_to_f32(bs[((kt_) * C::BK + 32) / group]);                          \
+        } else {                                                                               \
+            _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rb[j_] =                          \
+                *reinterpret_cast<const u32x4 *>(bb + (kt_) * C::BK + 8 * j_);                 \
+        }                                                                                      \
+    } while (0)
+#define COLI_SSTORE16(buf_)                                                                    \
+    do {                                                                                       \
+        uint16_t *sa_ = lds + (buf_) * C::STAGE;                                               \
+        uint16_t *sb_ = sa_ + C::BM * C::BK;                                                   \
+        _Pragma("unroll") for (int i_ = 0; i_ < C::A_PER_T; ++i_) {                            \
+            const int c_ = tid + i_ * C::NT;                                                   \
+            if (C::A_CHUNKS % C::NT == 0 || c_ < C::A_CHUNKS)                                  \
+                *reinterpret_cast<u32x4 *>(sa_ + swz(c_ >> 3, ch0)) = bf16x8_to_f16x8(ra[i_]); \
+        }                                                                                      \
+        if (i4) {                                                                              \
+            _Pragma("unroll") for (int c_ = 0; c_ < 8; ++c_)                                   \
+                *reinterpret_cast<u32x4 *>(sb_ + swz(tid, c_)) =                               \
+                    int4x8_to_f16x8(rq[c_ >> 2][c_ & 3], c_ < 4 ? s0 : s1);                    \
+        } else {                                                                               \
+            _Pragma("unroll") for (int c_ = 0; c_ < 8; ++c_)                                   \
+                *reinterpret_cast<u32x4 *>(sb_ + swz(tid, c_)) = bf16x8_to_f16x8(rb[c_]);      \
+        }                                                                                      \
+    } while (0)
+
+#pragma unroll
+    for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+        for (int n = 0; n < C::FN; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+
+    f16x8 af[2][C::FM], bfr[2][C::FN];
+#define COLI_LFRAG16(stage_, kk_, slot_)                                                       \
+    do {                                                                                       \
+        const uint16_t *sa_ = lds + (stage_) * C::STAGE;                                       \
+        const uint16_t *sb_ = sa_ + C::BM * C::BK;                                             \
+        const int ch_ = (kk_) * 2 + (lane >> 5);                                               \
+        _Pragma("unroll") for (int m_ = 0; m_ < C::FM; ++m_) af[slot_][m_] =                   \
+            *reinterpret_cast<const f16x8 *>(sa_ + swz((wm * C::FM + m_) * 32 + (lane & 31), ch_)); \
+        _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_) bfr[slot_][n_] =                  \
+            *reinterpret_cast<const f16x8 *>(sb_ + swz((wn * C::FN + n_) * 32 + (lane & 31), ch_)); \
+    } while (0)
+
+    const int nk = K / C::BK;
+    COLI_GLOAD16(0);
+    COLI_SSTORE16(0);
+    __syncthreads();
+    COLI_LFRAG16(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) COLI_GLOAD16(kt + 1);
+#pragma unroll
+        for (int kk = 0; kk < C::BK / 16; ++kk) {
+            const int slot = kk & 1;
+            if (kk + 1 < C::BK / 16) COLI_LFRAG16(cur, kk + 1, slot ^ 1);
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+                for (int n = 0; n < C::FN; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[slot][m], bfr[slot][n],
+                                                                       acc[m][n], 0, 0, 0);
+        }
+        if (kt + 1 < nk) {
+            COLI_SSTORE16(cur ^ 1);
+            __syncthreads();
+            COLI_LFRAG16(cur ^ 1, 0, 0);
+        }
+    }
+#undef COLI_GLOAD16
+#undef COLI_SSTORE16
+#undef COLI_LFRAG16
+}
+
+// ---------------------------------------------------------------------------
 // Direct-to-LDS tile engine (large tiles)
 //
 // Same contract as mfma_mainloop, but the tiles travel from global memory

@@ -258,6 +258,118 @@ __global__ __launch_bounds__(256) void down_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 1'/2'. int4 routed experts: the same grouped GEMMs on the fp16 engine, the
+// weight rows dequantised while they are staged into LDS.  The shared
+// expert (bf16) shares the gate+up launch: its tiles stage bf16 rows instead.
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ __launch_bounds__(256) void gateup_int4_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ gate_q, const uint16_t *__restrict__ gate_s,
+    const uint8_t *__restrict__ up_q, const uint16_t *__restrict__ up_s, int group,
+    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
+    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
+    int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+{
+    static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+    constexpr int FC = C::BN / 2;
+    const int t = xcd_tile(n_items[1]);
+    if (t < 0) return;
+    const int4 item = list[t];
+    const int nt = item.z;
+    const int R = T * K;
+    const ExpertTile et = decode_tile(item, count, offset, E, T, R);
+    const int f0 = nt * FC;
+    const int ch0 = threadIdx.x & 7;
+
+    const uint16_t *ap[C::A_PER_T];
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) {
+        int r = et.m0 + a_chunk_row<C>(i);
+        if (a_chunk_row<C>(i) >= C::BM || r >= et.cnt) r = et.m0;
+        const int tok = et.shared ? r : perm[et.base + r] / K;
+        ap[i] = x + (size_t)tok * D + ch0 * 8;
+    }
+    // this thread's B row: block b = row >> 5 holds gate (b even) or up (b odd)
+    const int brow = threadIdx.x, blk = brow >> 5;
+    const int f = min(f0 + (blk >> 1) * 32 + (brow & 31), F - 1);
+    const uint16_t *bb = nullptr;
+    const uint8_t *bq = nullptr;
+    const uint16_t *bs = nullptr;
+    if (et.shared) {
+        bb = ((blk & 1) ? s_up : s_gate) + (size_t)f * D;
+    } else {
+        const size_t row = (size_t)et.e * F + f;
+        bq = ((blk & 1) ? up_q : gate_q) + row * (D / 2);
+        bs = ((blk & 1) ? up_s : gate_s) + row * (D / group);
+    }
+    f32x16 acc[C::FM][C::FN];
+    mfma_mainloop_f16<C>(ap, bb, bq, bs, group, D, lds, acc);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
+#pragma unroll
+    for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+        for (int n = 0; n < C::FN; n += 2) {
+            const int fo = f0 + ((wn * C::FN + n) >> 1) * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
+                if (r < et.cnt && fo < F)
+                    h[(size_t)(et.base + r) * F + fo] =
+                        f32_to_bf16_bits(swiglu_clamped(acc[m][n][i], acc[m][n + 1][i]));
+            }
+        }
+}
+
+template <class C>
+__global__ __launch_bounds__(256) void down_int4_kernel(
+    const uint16_t *__restrict__ h, const uint8_t *__restrict__ down_q, const uint16_t *__restrict__ down_s,
+    int group, const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int F,
+    uint16_t *__restrict__ o)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+    const int t = xcd_tile(n_items[0]);
+    if (t < 0) return;
+    const int4 item = list[t];
+    const int e = item.x, m0 = item.y, nt = item.z;
+    const int cnt = count[e];
+    const int base = offset[e];
+    const int d0 = nt * C::BN;
+    const int ch0 = threadIdx.x & 7;
+
+    const uint16_t *ap[C::A_PER_T];
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) {
+        int rr = a_chunk_row<C>(i);
+        int r = (rr < C::BM && m0 + rr < cnt) ? m0 + rr : m0;
+        ap[i] = h + (size_t)(base + r) * F + ch0 * 8;
+    }
+    const int d = min(d0 + (int)threadIdx.x, D - 1);
+    const size_t row = (size_t)e * D + d;
+    f32x16 acc[C::FM][C::FN];
+    mfma_mainloop_f16<C>(ap, nullptr, down_q + row * (F / 2), down_s + row * (F / group), group, F, lds,
+                         acc);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
+#pragma unroll
+    for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+        for (int n = 0; n < C::FN; ++n) {
+            const int dd = d0 + acc_col<C>(wn, n, lane);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = m0 + acc_row<C>(wm, m, lane, i);
+                if (r < cnt && dd < D) o[(size_t)(base + r) * D + dd] = f32_to_bf16_bits(acc[m][n][i]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // 3. shared down GEMM over the tokens with the combine in the epilogue:
 //    v = S(x_t)[d]; v = fmaf(w_tj, o[inv(t,j)][d], v) for j = 0..K-1;
 //    y = residual + v.
@@ -479,6 +591,24 @@ static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     launch_combine(a, mk, st);
 }
 
+template <class C>
+static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
+{
+    const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
+    const long grid_gu = ((mt * ffn_col_tiles_gu(a.F) + 7) / 8) * 8;
+    const long grid_dn = ((mt * ffn_col_tiles_dn(a.D) + 7) / 8) * 8;
+    mk.mark(st);
+    gateup_int4_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
+        (const uint16_t *)a.x, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.list_gu,
+        a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+    mk.mark(st);
+    down_int4_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
+        (const uint16_t *)a.h, a.down_q, a.down_s, a.group, a.count, a.offset, a.list_dn, a.n_items,
+        a.D, a.F, (uint16_t *)a.o);
+    launch_combine(a, mk, st);
+}
+
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
 {
     const int T = a.T, D = a.D, K = a.K, F = a.F;
@@ -489,10 +619,16 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
     if (a.bf16) {
         ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, T, a.bm, ffn_col_tiles_gu(F),
                                              ffn_col_tiles_dn(D), a.list_gu, a.list_dn, a.n_items);
-        if (a.bm == SmallCfg::BM)
+        if (a.use_int4) {
+            if (a.bm == SmallCfg::BM)
+                launch_staged_int4<SmallCfg>(a, mk, st);
+            else
+                launch_staged_int4<LargeCfg>(a, mk, st);
+        } else if (a.bm == SmallCfg::BM) {
             launch_staged<SmallCfg>(a, mk, st);
-        else
+        } else {
             launch_staged<LargeCfg>(a, mk, st);
+        }
     } else {
         const int64_t n1 = (int64_t)(R + T) * F, n2 = (int64_t)R * D, n3 = (int64_t)T * D;
         mk.mark(st);

@@ -43,6 +43,10 @@ struct FfnLaunch {
     const float *w;
     const int32_t *count, *offset, *perm, *inv;
     const void *gate, *up, *down, *s_gate, *s_up, *s_down;
+    bool use_int4;         // routed experts in int4 (then gate/up/down above are unused)
+    const uint8_t *gate_q, *up_q, *down_q;
+    const uint16_t *gate_s, *up_s, *down_s;
+    int group;
     const float *residual;
     float *y;
     void *y_bf16;

@@ -48,9 +48,9 @@ def run_gpu(W, cfg, device="cuda"):
     return out
 
 
-def _oracle_mats(W):
+def _oracle_mats(W, cfg):
     if "gate_q" in W:
-        G = W.get("group", 32)
+        G = cfg.get("group", 32)
         return (oracle.Mat.int4(W["gate_q"], W["gate_s"], G),
                 oracle.Mat.int4(W["up_q"], W["up_s"], G),
                 oracle.Mat.int4(W["down_q"], W["down_s"], G))
@@ -58,7 +58,7 @@ def _oracle_mats(W):
 
 
 def run_oracle(W, cfg, tokens=None):
-    g, u, d = _oracle_mats(W)
+    g, u, d = _oracle_mats(W, cfg)
     return oracle.moe_layer(W["x"], W["wr"], W["bias"], g, u, d, W["s_gate"], W["s_up"],
                             W["s_down"], cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"],
                             tokens=tokens)

@@ -130,6 +130,14 @@ def test_int4_rejects_fp32_and_null():
                                        None, fake(5), None, fake(4), 1 << 31, None) == E_NULL
 
 
+def test_int4_rejects_bad_groups():
+    cs = _shape().c()
+    for g in (0, 16, 48, 4096):
+        w = CWeightsInt4(*([fake(50 + i) for i in range(6)] + [g] + [fake(60 + i) for i in range(3)]))
+        assert pkg.lib().coli_moe_ffn_int4(C.byref(cs), fake(1), C.byref(_routing()), C.byref(w),
+                                           None, fake(5), None, fake(4), 1 << 31, None) == E_SHAPE
+
+
 def test_valid_call_without_gpu_reports_device_error():
     # Only meaningful on a host with no GPU: there the last host check, the
     # device query, fails.  Never run it where a GPU could receive the fake

@@ -81,6 +81,39 @@ def test_prefill_bf16_sampled():
 
 
 # ---------------------------------------------------------------------------
+# int4 routed experts (offset-binary nibbles, fp16 group scales)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cid,T,D,E,K,F,group", [
+    (131, 100, 256, 40, 8, 192, 32),     # ~20 rows/expert: 32-row tiles, ragged columns
+    (132, 300, 128, 20, 8, 128, 32),     # ~120 rows/expert: 64-row tiles
+    (133, 57, 256, 24, 8, 128, 64),      # group of 64
+])
+def test_int4_small_shapes(cid, T, D, E, K, F, group):
+    cfg = custom_cfg(cid, T, D, E, K, F, "bf16", int4=True, group=group)
+    W = make_inputs(cfg)
+    _report(f"int4 cid={cid}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label=f"int4 cid={cid}"))
+
+
+def test_int4_workload_sampled():
+    import oracle
+    cfg = synth.CONFIGS["int4"]
+    W = synth.workload("int4")
+    got = run_gpu(W, cfg)
+    T, D, E, K, F, G = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], cfg["group"]
+    z = oracle.router_logits(W["x"], W["wr"], W["bias"], T, D, E)
+    ids, w = oracle.select_topk(z, K)
+    count, offset, perm, inv = oracle.permutation(ids, E)
+    toks = sample_tokens(ids, count, T)
+    Mi = oracle.Mat.int4
+    y = oracle.moe_ffn(W["x"], ids, w, Mi(W["gate_q"], W["gate_s"], G), Mi(W["up_q"], W["up_s"], G),
+                       Mi(W["down_q"], W["down_s"], G), W["s_gate"], W["s_up"], W["s_down"],
+                       T, D, E, K, F, tokens=toks)
+    ref = dict(ids=ids, w=w, count=count, offset=offset, perm=perm, inv=inv, y=y)
+    _report(f"int4 workload ({len(toks)} sampled tokens)",
+            compare(got, ref, cfg, tokens=toks, label="int4"))
+
+
+# ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cid,T,D,E,K,F,dt", [
