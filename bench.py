@@ -38,6 +38,8 @@ WORKLOAD_NAMES = {
     "decode": "decode T=64, D=2048, F=768, 288 experts top-8 + 1 shared, bf16",
     "int4": "int4 experts T=512, D=2048, F=768, 288 experts top-8 + 1 shared, group 32",
     "tiny": "tiny T=8, D=128, F=64, 288 experts top-8 + 1 shared, fp32",
+    "stacked": "stacked decode: 42 MoE layers, T=256, D=2048, F=768, 288 experts top-8 + 1 shared, "
+               "bf16, fp32 residual stream",
 }
 
 
@@ -286,6 +288,80 @@ def run_workload(name, steps, warmup, hip):
 
 
 # ---------------------------------------------------------------------------
+# stacked decode: 42 layers in sequence, residual add between layers
+# ---------------------------------------------------------------------------
+def run_stacked(steps, warmup, hip):
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_moe_ffn_coli_amd import COLI_BF16
+    from sparse_moe_ffn_coli_amd.layer import DeviceLayer, to_device
+
+    cfg = synth.CONFIGS["stacked"]
+    T, D, E, K, F, L = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], cfg["layers"]
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        W = synth.layer_weights(cfg, l)
+        layers.append(DeviceLayer(W, T, D, E, K, F, COLI_BF16))
+        del W
+        if l % 6 == 5 or l == L - 1:
+            log(f"stacked: {l + 1}/{L} layers generated and resident ({time.time() - t0:.0f}s)")
+    x0 = to_device(synth.x_rows(cfg, synth.load_attempts("stacked"))).view(torch.bfloat16)
+    xb = [torch.empty_like(x0), torch.empty_like(x0)]
+    xf = torch.empty((T, D), dtype=torch.float32, device=x0.device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(gu_events=None):
+        # the residual stream starts from x0 every step; layer l reads bf16(x_l)
+        xb[0].copy_(x0)
+        xf.copy_(x0)
+        cur = 0
+        for l, layer in enumerate(layers):
+            ev = None if gu_events is None else [None, gu_events[2 * l], gu_events[2 * l + 1]]
+            layer(xb[cur], y=xf, residual=xf, y_bf16=xb[1 - cur], ffn_events=ev)
+            cur ^= 1
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    gu = hip.events(2 * L * steps)
+    start, stop = hip.events(2)
+    h0 = time.perf_counter()
+    hip.record(start, stream)
+    for i in range(steps):
+        step(gu[2 * L * i:2 * L * (i + 1)])
+    hip.record(stop, stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    total_ms = hip.elapsed_ms(start, stop)
+    gu_ms = [hip.elapsed_ms(gu[2 * j], gu[2 * j + 1]) for j in range(L * steps)]
+    hip.destroy(gu + [start, stop])
+    step_s = total_ms / steps / 1e3
+    log(f"stacked: {steps} timed steps, {step_s * 1e3:.3f} ms per 42-layer pass")
+
+    flops = nbytes = gu_flops = gu_bytes = 0
+    n_es = []
+    for layer in layers:
+        st, fl, nb, n_e = algorithmic(cfg, layer.routing.count.cpu().numpy())
+        flops, nbytes = flops + fl, nbytes + nb
+        gu_flops, gu_bytes = gu_flops + st["gate_up"]["flops"], gu_bytes + st["gate_up"]["bytes"]
+        n_es.append(n_e)
+    gu_s = sum(gu_ms) / len(gu_ms) / 1e3
+    res = dict(cfg=cfg, step_s=step_s, host_step_s=host_s / steps, tokens_per_s=T / step_s,
+               n_e=round(sum(n_es) / len(n_es), 1), flops=flops, bytes=nbytes, gu_s=gu_s,
+               stage_us={}, roofline=roofline(gu_flops / L, gu_bytes / L, gu_s, PEAK_BF16_FLOPS),
+               gate_up_work=dict(flops=gu_flops // L, bytes=gu_bytes // L),
+               mfma_pct=round(100 * flops / step_s / PEAK_BF16_FLOPS, 2),
+               hbm_gbs=round(nbytes / step_s / 1e9, 1),
+               hbm_pct=round(100 * nbytes / step_s / PEAK_HBM, 2))
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 def cpu_baseline(name, budget_s=15.0):
@@ -296,6 +372,8 @@ def cpu_baseline(name, budget_s=15.0):
 
     cfg = synth.CONFIGS[name]
     T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
+    if name == "stacked":
+        return cpu_baseline_stacked(budget_s)
     W = synth.workload(name)
     if cfg.get("int4"):
         G = cfg["group"]
@@ -321,6 +399,31 @@ def cpu_baseline(name, budget_s=15.0):
     return {"value": round(n / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of the {T} tokens of the {name} workload: router over all "
                       f"{E} experts, top-{K}, routed + shared FFN, in fp64 ({el:.1f} s)"}
+
+
+def cpu_baseline_stacked(budget_s):
+    """The oracle's chain over the 42 layers for the first n tokens (weights
+    regenerated per layer; only the oracle's own time is counted)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    cfg = synth.CONFIGS["stacked"]
+    T, D, E, K, F, L = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], cfg["layers"]
+    n = max(1, oracle.num_threads())
+    x0 = synth.x_rows(cfg, synth.load_attempts("stacked"))[:n]
+    x = (x0.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    el = 0.0
+    for l in range(L):
+        W = synth.layer_weights(cfg, l)
+        t = time.perf_counter()
+        x = oracle.residual_layer(x, W["wr"], W["bias"], W["gate"], W["up"], W["down"],
+                                  W["s_gate"], W["s_up"], W["s_down"], D, E, K, F)[5]
+        el += time.perf_counter() - t
+    return {"value": round(n / el, 3), "unit": "tokens/s (42-layer pass)", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"first {n} of the {T} tokens through all {L} layers in fp64 "
+                                        f"({el:.1f} s of oracle time)"}
 
 
 def main():
@@ -353,7 +456,10 @@ def main():
     if args.copy_calibration:
         copy_calibration()
 
-    main_res = run_workload(args.workload, args.steps, args.warmup, hip)
+    if args.workload == "stacked":
+        main_res = run_stacked(args.steps, args.warmup, hip)
+    else:
+        main_res = run_workload(args.workload, args.steps, args.warmup, hip)
     dec = None
     if args.workload == "prefill" and not args.no_decode:
         dec = run_workload("decode", args.steps, args.warmup, hip)
@@ -365,8 +471,9 @@ def main():
 
     cfg = main_res["cfg"]
     out = {
-        "metric": f"routed-MoE tokens/s ({args.workload})" if args.workload != "prefill"
-                  else "routed-MoE tokens/s at T=4096 prefill",
+        "metric": ("routed-MoE tokens/s at T=4096 prefill" if args.workload == "prefill" else
+                   "routed-MoE tokens/s, 42-layer stacked decode (T=256)" if args.workload == "stacked"
+                   else f"routed-MoE tokens/s ({args.workload})"),
         "value": round(main_res["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
