@@ -240,41 +240,52 @@ __device__ __forceinline__ void mfma_mainloop(const uint16_t *const (&ap)[C::A_P
 //         of byte i, value (nibble - 8) * scale with one fp16 scale per
 //         `group` consecutive elements (offset-binary, "feat(glm53): add
 //         device-resident HIP backend for MI350P", section "Key changes");
-//         the product is formed in fp32 (exact) and rounded once to fp16;
 //   bf16: converted like the A rows (the shared expert's dense weights).
+//
+// Both operands are stored with the same order of K inside every 16-byte
+// chunk of 8 elements, 0,4,1,5,2,6,3,7: dword j holds elements j and j + 4.
+// A dot product over the chunk does not depend on that order, and it lets
+// one AND/OR put two nibbles of a 32-bit word (bits 4j and 16 + 4j) under the
+// fp16 exponent of 1024: the pair is then 1024 + n exactly, subtracting 1032
+// leaves n - 8 exactly, and one fp16 multiply by the scale rounds the exact
+// product (n - 8) * scale once, as an fp32 product rounded to fp16 would.
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// 8 bf16 (elements 0..7) -> 8 fp16 in the chunk order 0,4,1,5,2,6,3,7
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v)
 {
     u32x4 r;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const _Float16 lo = (_Float16)__uint_as_float(v[k] << 16);
-        const _Float16 hi = (_Float16)__uint_as_float(v[k] & 0xffff0000u);
-        r[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    return r;
-}
-
-// 8 nibbles (elements 0..7 of a chunk; element 2i in the low nibble of byte i)
-// -> 8 fp16 values (nibble - 8) * scale
-__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, float scale)
-{
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float a = (float)((int)((w >> (8 * k)) & 0xF) - 8) * scale;
-        const float b = (float)((int)((w >> (8 * k + 4)) & 0xF) - 8) * scale;
-        r[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t p = v[j >> 1], q = v[2 + (j >> 1)];
+        const float a = __uint_as_float((j & 1) ? (p & 0xffff0000u) : (p << 16));
+        const float b = __uint_as_float((j & 1) ? (q & 0xffff0000u) : (q << 16));
+        r[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
     }
     return r;
 }
 
-__device__ __forceinline__ float fp16_bits_to_f32(uint16_t h)
+// 8 nibbles of w (element p in bits 4p..4p+3) -> 8 fp16 values
+// (nibble - 8) * scale in the chunk order 0,4,1,5,2,6,3,7
+__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, f16x2 scale2)
 {
-    return (float)__builtin_bit_cast(_Float16, h);
+    const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t d = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+        const f16x2 v = (__builtin_bit_cast(f16x2, d) - off) * scale2;
+        r[j] = __builtin_bit_cast(uint32_t, v);
+    }
+    return r;
+}
+
+__device__ __forceinline__ f16x2 fp16_bits_splat(uint16_t h)
+{
+    return __builtin_bit_cast(f16x2, (uint32_t)h * 0x00010001u);
 }
 
 // ap: A rows (bf16) as in mfma_mainloop.  B row of this thread (row tid):
@@ -296,7 +307,7 @@ __device__ __forceinline__ void mfma_mainloop_f16(const uint16_t *const (&ap)[C:
     u32x4 ra[C::A_PER_T];
     u32x4 rq[2];
     u32x4 rb[8];
-    float s0 = 0.f, s1 = 0.f;
+    f16x2 s0 = {}, s1 = {};
 #define COLI_GLOAD16(kt_)                                                                      \
     do {                                                                                       \
         _Pragma("unroll") for (int i_ = 0; i_ < C::A_PER_T; ++i_) ra[i_] =                     \
@@ -304,8 +315,8 @@ __device__ __forceinline__ void mfma_mainloop_f16(const uint16_t *const (&ap)[C:
         if (i4) {                                                                              \
             rq[0] = *reinterpret_cast<const u32x4 *>(bq + (kt_) * (C::BK / 2));                \
             rq[1] = *reinterpret_cast<const u32x4 *>(bq + (kt_) * (C::BK / 2) + 16);           \
-            s0 = fp16_bits_to_f32(bs[((kt_) * C::BK) / group]);                               \
-            s1 = fp16_bits_to_f32(bs[((kt_) * C::BK + 32) / group]);                          \
+            s0 = fp16_bits_splat(bs[((kt_) * C::BK) / group]);                                   \
+            s1 = fp16_bits_splat(bs[((kt_) * C::BK + 32) / group]);                              \
         } else {                                                                               \
             _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rb[j_] =                          \
                 *reinterpret_cast<const u32x4 *>(bb + (kt_) * C::BK + 8 * j_);                 \
