@@ -53,14 +53,13 @@ RouteWs route_ws(const coli_moe_shape *s)
     return w;
 }
 
-FfnWs ffn_ws(const coli_moe_shape *s, int int4)
+FfnWs ffn_ws(const coli_moe_shape *s, int quant)
 {
-    (void)int4;
     FfnWs w{};
     const size_t T = (size_t)s->T, K = (size_t)s->K, D = (size_t)s->D, F = (size_t)s->F;
     const size_t R = T * K;
     const size_t elt = (s->dtype == COLI_F32) ? 4 : 2;
-    w.bm = coli::ffn_tile_rows(s->T, s->E, s->K);
+    w.bm = coli::ffn_tile_rows(s->T, s->E, s->K, quant);
     const size_t max_tiles = (size_t)coli::ffn_max_tiles(s->T, s->E, s->K, w.bm);
     w.h = 0;
     w.o = align_up(w.h + (R + T) * F * elt);

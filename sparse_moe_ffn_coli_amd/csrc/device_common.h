@@ -1,6 +1,8 @@
 // device_common.h -- device helpers shared by the gfx950 kernels of the routed
 // MoE FFN layer: bf16 conversions, the clamped SwiGLU, and the LDS-staged
-// bf16 MFMA tile engine used by every matrix product of the layer.
+// MFMA tile engines behind every matrix product of the layer (a register-
+// staged engine for row-light tiles and its fp16/int4 variant, and a
+// 256 x 256 engine with direct global->LDS copies for row-heavy tiles).
 //
 // Activation: clamped SwiGLU, gate limited from above at 10 before the SiLU
 // and up limited to [-10, 10] ("Add GLM-5.3-Flash (glm5next) support with
@@ -230,6 +232,172 @@ __device__ __forceinline__ void mfma_mainloop(const uint16_t *const (&ap)[C::A_P
 }
 
 // ---------------------------------------------------------------------------
+// Large-tile engine: 256 x 256 blocks, eight waves, both operands copied from
+// global memory straight into LDS (global_load_lds_dwordx4) through a ring of
+// NS stages, NS - 1 of them in flight.
+//
+// Sized for the row-heavy products (many tokens per expert), whose operands
+// come mostly from beyond L2 (weights from HBM, gathered activation rows
+// from the memory-side cache): a stage is one reduction step of BK elements
+// for 256 A rows and 256 B rows, and keeping NS - 1 stages in flight per CU
+// (up to 128 KB) is what covers that latency.  Copy instruction q (0..31 for
+// A, 32..63 for B) fills LDS bytes 1024 q .. +1023 of the stage with rows
+// RPI q .. RPI q + RPI - 1 of its operand (RPI = 1024 / (2 BK) rows of
+// 2 BK bytes); lane l fetches 16 bytes of row RPI q + l / CPR (CPR = BK / 8
+// chunks per row), and the source chunk is chosen so that the lane's LDS
+// slot holds the swizzled layout read below (chunk c of row r at position
+// c ^ ((r >> 1) & 7) for BK = 64, c ^ ((r >> 2) & 3) for BK = 32; either
+// makes the 16-lane fragment reads free of bank conflicts).  Wave w issues
+// instructions j * 8 + w.
+//
+// Step kt: wait until this wave's copies of stage kt have landed (vmcnt),
+// barrier (everyone's have, and everyone has left step kt-1), issue stage
+// kt + NS - 1 into the buffer read in step kt-1, then the MFMAs of stage kt.
+//
+// Waves form a 4 x 2 grid, each owning 64 rows x 128 columns (2 x 4
+// fragments of 32 x 32, v_mfma_f32_32x32x16_bf16); two waves fit per SIMD.
+//
+// NFW = fragments of this wave that hold real rows (0..2), chosen by the
+// caller per wave from the tile's row count: fragments without real rows
+// are neither read from LDS nor multiplied.  `valid` = real A rows of the
+// tile: A copies whose rows all lie past it are skipped with NS = 2 (every
+// step then waits for all of the wave's copies, so the count need not be
+// fixed); with a deeper ring they run, rereading a real row.
+// ---------------------------------------------------------------------------
+template <int BK_, int NS_>
+struct BigCfgT {
+    static constexpr int NT = 512, BM = 256, BN = 256, BK = BK_, NS = NS_;
+    static constexpr int WAVES_M = 4, WAVES_N = 2, FM = 2, FN = 4;
+    static constexpr int CPR = BK / 8;                       // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;                     // rows per copy instruction
+    static constexpr int OPERAND_BYTES = 256 * BK * 2;
+    static constexpr int STAGE_BYTES = 2 * OPERAND_BYTES;
+    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+    static constexpr int CPO = 256 / RPI / 8;                // copies per wave per operand per stage
+    static constexpr int CPW = 2 * CPO;                      // copies per wave per stage
+    static_assert(BK == 32 || BK == 64, "row of 64 or 128 bytes");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(NS >= 2 && (NS - 1) * CPW <= 63, "vmcnt range");
+};
+using BigCfg = BigCfgT<64, 2>;
+
+// Tile row (within its A or B region) fetched by this lane in copy j of wave w.
+template <class C>
+__device__ __forceinline__ int big_copy_row(int j, int w)
+{
+    return ((j % C::CPO) * 8 + w) * C::RPI + (threadIdx.x & 63) / C::CPR;
+}
+template <class C>
+__device__ __forceinline__ int big_swz_pos(int row, int c)
+{
+    return (C::BK == 64) ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
+}
+// Source chunk of that lane (its LDS slot is chunk position lane % CPR of the row).
+template <class C>
+__device__ __forceinline__ int big_copy_chunk(int row)
+{
+    return big_swz_pos<C>(row, (threadIdx.x & 63) % C::CPR);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `pending` stages of this wave's copies are in flight.
+template <class C, int P>
+__device__ __forceinline__ void big_wait_stages(int pending)
+{
+    if constexpr (P == 0) {
+        wait_vmcnt_c<0>();
+    } else {
+        if (pending >= P) wait_vmcnt_c<P * C::CPW>();
+        else big_wait_stages<C, P - 1>(pending);
+    }
+}
+
+// rp[j]: this lane's source for copy j at k = 0 (row big_copy_row(j, w),
+// chunk big_copy_chunk(row) already applied; j < CPO: A, else B), readable
+// for every k < K.  w = this wave (0..7), wm = w >> 1, wn = w & 1.
+template <class C, int NFW>
+__device__ __forceinline__ void big_mainloop(const uint16_t *const (&rp)[C::CPW], int K, int valid, int w,
+                                             char *lds, f32x16 (&acc)[C::FM][C::FN])
+{
+    const int lane = threadIdx.x & 63;
+    const int wm = w >> 1, wn = w & 1;
+    const int nk = K / C::BK;
+
+#pragma unroll
+    for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+        for (int n = 0; n < C::FN; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+
+#define COLI_BIG_ISSUE(kt_)                                                                    \
+    do {                                                                                       \
+        char *st_ = lds + ((kt_) % C::NS) * C::STAGE_BYTES;                                    \
+        _Pragma("unroll") for (int j_ = 0; j_ < C::CPW; ++j_)                                  \
+            if (C::NS > 2 || j_ >= C::CPO || ((j_ % C::CPO) * 8 + w) * C::RPI < valid)         \
+            __builtin_amdgcn_global_load_lds(                                                  \
+                (const __attribute__((address_space(1))) void *)(rp[j_] + (kt_) * C::BK),     \
+                (__attribute__((address_space(3))) void *)(st_ + (j_ / C::CPO) * C::OPERAND_BYTES + \
+                                                           ((j_ % C::CPO) * 8 + w) * 1024),    \
+                16, 0, 0);                                                                     \
+    } while (0)
+
+    bf16x8 af[2][C::FM], bfr[2][C::FN];
+#define COLI_BIG_LFRAG(st_, kk_, slot_)                                                        \
+    do {                                                                                       \
+        const int c_ = (kk_) * 2 + (lane >> 5);                                                \
+        _Pragma("unroll") for (int m_ = 0; m_ < NFW; ++m_) {                                   \
+            const int r_ = (wm * C::FM + m_) * 32 + (lane & 31);                               \
+            af[slot_][m_] = *reinterpret_cast<const bf16x8 *>(                                 \
+                (st_) + (r_ * C::CPR + big_swz_pos<C>(r_, c_)) * 16);                          \
+        }                                                                                      \
+        _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_) {                                 \
+            const int r_ = (wn * C::FN + n_) * 32 + (lane & 31);                               \
+            bfr[slot_][n_] = *reinterpret_cast<const bf16x8 *>(                                \
+                (st_) + C::OPERAND_BYTES + (r_ * C::CPR + big_swz_pos<C>(r_, c_)) * 16);       \
+        }                                                                                      \
+    } while (0)
+
+#pragma unroll
+    for (int s = 0; s < C::NS - 1; ++s)
+        if (s < nk) COLI_BIG_ISSUE(s);
+    for (int kt = 0; kt < nk; ++kt) {
+        // stages issued after kt that may still be in flight
+        big_wait_stages<C, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
+        // A bare barrier: __syncthreads() would also wait for the copies
+        // still in flight (its memory fence covers them).  Every LDS read of
+        // the previous step has been consumed by an MFMA before this point,
+        // and the memory clobber keeps the compiler from moving LDS accesses
+        // across it.
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + C::NS - 1 < nk) COLI_BIG_ISSUE(kt + C::NS - 1);
+        if (NFW > 0) {
+            const char *st = lds + (kt % C::NS) * C::STAGE_BYTES;
+            COLI_BIG_LFRAG(st, 0, 0);
+#pragma unroll
+            for (int kk = 0; kk < C::BK / 16; ++kk) {
+                const int slot = kk & 1;
+                if (kk + 1 < C::BK / 16) COLI_BIG_LFRAG(st, kk + 1, slot ^ 1);
+#pragma unroll
+                for (int m = 0; m < NFW; ++m)
+#pragma unroll
+                    for (int n = 0; n < C::FN; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][m], bfr[slot][n],
+                                                                            acc[m][n], 0, 0, 0);
+            }
+        }
+    }
+#undef COLI_BIG_ISSUE
+#undef COLI_BIG_LFRAG
+}
+
+// ---------------------------------------------------------------------------
 // fp16 variant of the register-staged engine, for int4 weights
 //
 // Operands are fp16 in LDS and multiplied with v_mfma_f32_32x32x16_f16 (fp32
@@ -388,166 +556,6 @@ __device__ __forceinline__ void mfma_mainloop_f16(const uint16_t *const (&ap)[C:
 #undef COLI_GLOAD16
 #undef COLI_SSTORE16
 #undef COLI_LFRAG16
-}
-
-// ---------------------------------------------------------------------------
-// Direct-to-LDS tile engine (large tiles)
-//
-// Same contract as mfma_mainloop, but the tiles travel from global memory
-// straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at
-// M0 + 16 * lane), so no VGPRs are spent on staging and NS stages of BK = 32
-// can be in flight at once (a ring of NS LDS buffers).  A stage holds the
-// BM A rows followed by the BN B rows, 64 bytes (4 chunks) per row; chunk c
-// of row r sits at position c ^ ((r >> 2) & 3), which makes both the 1 KB
-// DMA writes and the 16-rows-per-cycle fragment reads bank-conflict free.
-// Load instruction j of wave w covers rows 16 (4 j + w) .. +15.
-//
-// `valid` = number of real A rows in the tile (1..BM).  A load instruction
-// whose 16 rows are all past `valid` is skipped, and so are the MFMAs and
-// LDS reads of a 32-row fragment past `valid`: a tile of a lightly loaded
-// expert costs little more than streaming its weight rows.  The per-wave
-// count of issued loads is uniform, so the vmcnt waits below stay exact.
-//
-// Per stage kt (frags of reduction step 0 already in registers):
-//   read frags of step 1 | MFMAs of step 0 |
-//   wait for stage kt+1 (own loads), barrier (everyone's loads landed and
-//   everyone left stage kt-1), issue stage kt+NS-1 into kt-1's buffer,
-//   read frags of stage kt+1 step 0 | MFMAs of step 1
-// ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NS_>
-struct DmaCfg {
-    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NS = NS_;
-    static constexpr int BK = 32;
-    static constexpr int FM = BM / (WAVES_M * 32);
-    static constexpr int FN = BN / (WAVES_N * 32);
-    static constexpr int ROWS = BM + BN;
-    static constexpr int LPW = ROWS / 64;               // load instructions per wave per stage
-    static constexpr int STAGE_BYTES = ROWS * 64;
-    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
-    static_assert(ROWS % 64 == 0 && BM % 16 == 0, "rows per stage");
-    static_assert(NS >= 3 && (NS & (NS - 1)) == 0, "stages");
-    static_assert(WAVES_M * WAVES_N == 4, "four waves");
-    static_assert(FM >= 1 && FN >= 1, "tile shape");
-};
-
-// Tile row covered by this lane in load instruction j, and the source chunk
-// it must fetch so that the DMA's lane-contiguous layout is the swizzled one.
-template <class C>
-__device__ __forceinline__ int dma_row(int j)
-{
-    return (j * 4 + (threadIdx.x >> 6)) * 16 + ((threadIdx.x & 63) >> 2);
-}
-__device__ __forceinline__ int dma_chunk(int row) { return (threadIdx.x & 3) ^ ((row >> 2) & 3); }
-
-// s_waitcnt vmcnt(n) with expcnt/lgkmcnt unconstrained (gfx9 encoding: vmcnt
-// in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).  n <= 47.
-__device__ __forceinline__ void wait_vmcnt(int n)
-{
-#define COLI_W(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
-    switch (n) {
-        COLI_W(0) COLI_W(1) COLI_W(2) COLI_W(3) COLI_W(4) COLI_W(5) COLI_W(6) COLI_W(7)
-        COLI_W(8) COLI_W(9) COLI_W(10) COLI_W(11) COLI_W(12) COLI_W(13) COLI_W(14) COLI_W(15)
-        COLI_W(16) COLI_W(17) COLI_W(18) COLI_W(19) COLI_W(20) COLI_W(21) COLI_W(22) COLI_W(23)
-        COLI_W(24) COLI_W(25) COLI_W(26) COLI_W(27) COLI_W(28) COLI_W(29) COLI_W(30) COLI_W(31)
-        COLI_W(32) COLI_W(33) COLI_W(34) COLI_W(35) COLI_W(36) COLI_W(37) COLI_W(38) COLI_W(39)
-        COLI_W(40) COLI_W(41) COLI_W(42) COLI_W(43) COLI_W(44) COLI_W(45) COLI_W(46) COLI_W(47)
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-#undef COLI_W
-}
-
-// rp[j]: this lane's source for load instruction j (its row, already offset
-// by dma_chunk), a valid readable address even for padding rows.
-template <class C>
-__device__ __forceinline__ void dma_mainloop(const uint16_t *const (&rp)[C::LPW], int K, int valid,
-                                             char *lds, f32x16 (&acc)[C::FM][C::FN])
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int nk = K / C::BK;
-
-    // load instructions this wave issues per stage (A instructions past
-    // `valid` are skipped; B instructions always run)
-    int nload = 0;
-#pragma unroll
-    for (int j = 0; j < C::LPW; ++j) {
-        const int q = j * 4 + wave;
-        nload += (q * 16 >= C::BM || q * 16 < valid) ? 1 : 0;
-    }
-
-#define COLI_ISSUE(kt_)                                                                          \
-    do {                                                                                         \
-        char *sb_ = lds + ((kt_) & (C::NS - 1)) * C::STAGE_BYTES;                               \
-        _Pragma("unroll") for (int j_ = 0; j_ < C::LPW; ++j_) {                                 \
-            const int q_ = j_ * 4 + wave;                                                        \
-            if (q_ * 16 >= C::BM || q_ * 16 < valid)                                            \
-                __builtin_amdgcn_global_load_lds(                                                \
-                    (const __attribute__((address_space(1))) void *)(rp[j_] + (kt_) * C::BK),  \
-                    (__attribute__((address_space(3))) void *)(sb_ + q_ * 1024), 16, 0, 0);     \
-        }                                                                                        \
-    } while (0)
-
-    bf16x8 af[2][C::FM], bfr[2][C::FN];
-#define COLI_LFRAG(kt_, kk_, slot_)                                                              \
-    do {                                                                                         \
-        const char *sa_ = lds + ((kt_) & (C::NS - 1)) * C::STAGE_BYTES;                         \
-        const char *sbb_ = sa_ + C::BM * 64;                                                     \
-        const int c_ = (kk_) * 2 + (lane >> 5);                                                 \
-        _Pragma("unroll") for (int m_ = 0; m_ < C::FM; ++m_) {                                  \
-            const int r_ = (wm * C::FM + m_) * 32 + (lane & 31);                                \
-            if ((wm * C::FM + m_) * 32 < valid)                                                  \
-                af[slot_][m_] = *reinterpret_cast<const bf16x8 *>(                               \
-                    sa_ + r_ * 64 + ((c_ ^ ((r_ >> 2) & 3)) << 4));                              \
-        }                                                                                        \
-        _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_) {                                  \
-            const int r_ = (wn * C::FN + n_) * 32 + (lane & 31);                                \
-            bfr[slot_][n_] = *reinterpret_cast<const bf16x8 *>(                                  \
-                sbb_ + r_ * 64 + ((c_ ^ ((r_ >> 2) & 3)) << 4));                                 \
-        }                                                                                        \
-    } while (0)
-#define COLI_MMA(slot_)                                                                          \
-    do {                                                                                         \
-        _Pragma("unroll") for (int m_ = 0; m_ < C::FM; ++m_)                                    \
-            if ((wm * C::FM + m_) * 32 < valid)                                                  \
-                _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_)                            \
-                    acc[m_][n_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                       \
-                        af[slot_][m_], bfr[slot_][n_], acc[m_][n_], 0, 0, 0);                    \
-    } while (0)
-
-#pragma unroll
-    for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-        for (int n = 0; n < C::FN; ++n)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
-#pragma unroll
-    for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) af[0][m][i] = af[1][m][i] = (__bf16)0.f;
-
-    // prologue: stages 0 .. NS-2 in flight; wait for stage 0
-#pragma unroll
-    for (int st = 0; st < C::NS - 1; ++st)
-        if (st < nk) COLI_ISSUE(st);
-    wait_vmcnt(min(C::NS - 2, nk - 1) * nload);
-    __syncthreads();
-    COLI_LFRAG(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        COLI_LFRAG(kt, 1, 1);
-        COLI_MMA(0);
-        if (kt + 1 < nk) {
-            wait_vmcnt((min(kt + C::NS - 2, nk - 1) - (kt + 1)) * nload);
-            __syncthreads();
-            if (kt + C::NS - 1 < nk) COLI_ISSUE(kt + C::NS - 1);
-            COLI_LFRAG(kt + 1, 0, 0);
-        }
-        COLI_MMA(1);
-    }
-    // leave LDS quiescent for the caller's epilogue
-    __syncthreads();
-#undef COLI_ISSUE
-#undef COLI_LFRAG
-#undef COLI_MMA
 }
 
 }  // namespace coli

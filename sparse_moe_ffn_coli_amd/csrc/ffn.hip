@@ -258,6 +258,124 @@ __global__ __launch_bounds__(256) void down_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 1/2 on the large-tile engine (row-heavy batches): 256 x 256 tiles, eight
+// waves.  Each wave runs the variant for its number of real 32-row fragments.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int big_wave_fragments(int rows, int wm)
+{
+    return min(max((rows - wm * 64 + 31) >> 5, 0), 2);
+}
+
+template <int NFW>
+__device__ __forceinline__ void gateup_big_body(const uint16_t *const (&rp)[BigCfg::CPW], const ExpertTile &et,
+                                                int f0, int D, int F, int w, char *lds,
+                                                uint16_t *__restrict__ h)
+{
+    f32x16 acc[BigCfg::FM][BigCfg::FN];
+    big_mainloop<BigCfg, NFW>(rp, D, min(et.cnt - et.m0, BigCfg::BM), w, lds, acc);
+    const int lane = threadIdx.x & 63, wm = w >> 1, wn = w & 1;
+#pragma unroll
+    for (int m = 0; m < NFW; ++m)
+#pragma unroll
+        for (int n = 0; n < BigCfg::FN; n += 2) {
+            const int f = f0 + (wn * 2 + (n >> 1)) * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = et.m0 + wm * 64 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (r < et.cnt && f < F)
+                    h[(size_t)(et.base + r) * F + f] =
+                        f32_to_bf16_bits(swiglu_clamped(acc[m][n][i], acc[m][n + 1][i]));
+            }
+        }
+}
+
+__global__ __launch_bounds__(512) void gateup_big_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
+    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
+    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
+    int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[BigCfg::LDS_BYTES];
+    const int t = xcd_tile(n_items[1]);
+    if (t < 0) return;
+    const int4 item = list[t];
+    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
+    const uint16_t *G = et.shared ? s_gate : gate + (size_t)et.e * F * D;
+    const uint16_t *U = et.shared ? s_up : up + (size_t)et.e * F * D;
+    const int f0 = item.z * (BigCfg::BN / 2);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint16_t *rp[BigCfg::CPW];
+#pragma unroll
+    for (int j = 0; j < BigCfg::CPO; ++j) {
+        const int row = big_copy_row<BigCfg>(j, w);
+        const int ch = big_copy_chunk<BigCfg>(row);
+        int r = et.m0 + row;                      // padding rows reread the tile's first row
+        if (r >= et.cnt) r = et.m0;
+        const int tok = et.shared ? r : perm[et.base + r] / K;
+        rp[j] = x + (size_t)tok * D + ch * 8;
+        rp[BigCfg::CPO + j] = gateup_b_row(G, U, f0, row, D, F) + ch * 8;
+    }
+    const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
+    if (nfw == 2) gateup_big_body<2>(rp, et, f0, D, F, w, lds, h);
+    else if (nfw == 1) gateup_big_body<1>(rp, et, f0, D, F, w, lds, h);
+    else gateup_big_body<0>(rp, et, f0, D, F, w, lds, h);
+}
+
+template <int NFW>
+__device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg::CPW], int m0, int cnt,
+                                              int base, int d0, int D, int F, int w, char *lds,
+                                              uint16_t *__restrict__ o)
+{
+    f32x16 acc[BigCfg::FM][BigCfg::FN];
+    big_mainloop<BigCfg, NFW>(rp, F, min(cnt - m0, BigCfg::BM), w, lds, acc);
+    const int lane = threadIdx.x & 63, wm = w >> 1, wn = w & 1;
+#pragma unroll
+    for (int m = 0; m < NFW; ++m)
+#pragma unroll
+        for (int n = 0; n < BigCfg::FN; ++n) {
+            const int d = d0 + (wn * BigCfg::FN + n) * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = m0 + wm * 64 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (r < cnt && d < D) o[(size_t)(base + r) * D + d] = f32_to_bf16_bits(acc[m][n][i]);
+            }
+        }
+}
+
+__global__ __launch_bounds__(512) void down_big_kernel(
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ down,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int F,
+    uint16_t *__restrict__ o)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[BigCfg::LDS_BYTES];
+    const int t = xcd_tile(n_items[0]);
+    if (t < 0) return;
+    const int4 item = list[t];
+    const int e = item.x, m0 = item.y;
+    const int cnt = count[e], base = offset[e];
+    const int d0 = item.z * BigCfg::BN;
+    const uint16_t *W = down + (size_t)e * D * F;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint16_t *rp[BigCfg::CPW];
+#pragma unroll
+    for (int j = 0; j < BigCfg::CPO; ++j) {
+        const int row = big_copy_row<BigCfg>(j, w);
+        const int ch = big_copy_chunk<BigCfg>(row);
+        int r = m0 + row;
+        if (r >= cnt) r = m0;
+        rp[j] = h + (size_t)(base + r) * F + ch * 8;
+        const int d = min(d0 + row, D - 1);       // rows past D reread the last one
+        rp[BigCfg::CPO + j] = W + (size_t)d * F + ch * 8;
+    }
+    const int nfw = big_wave_fragments(cnt - m0, w >> 1);
+    if (nfw == 2) down_big_body<2>(rp, m0, cnt, base, d0, D, F, w, lds, o);
+    else if (nfw == 1) down_big_body<1>(rp, m0, cnt, base, d0, D, F, w, lds, o);
+    else down_big_body<0>(rp, m0, cnt, base, d0, D, F, w, lds, o);
+}
+
+// ---------------------------------------------------------------------------
 // 1'/2'. int4 routed experts: the same grouped GEMMs on the fp16 engine, the
 // weight rows dequantised while they are staged into LDS.  The shared
 // expert (bf16) shares the gate+up launch: its tiles stage bf16 rows instead.
@@ -541,14 +659,17 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 // ---------------------------------------------------------------------------
 using SmallCfg = TileCfg<32, 256, 1, 4>;
 using LargeCfg = TileCfg<64, 256, 2, 2>;
+constexpr int BIG_BM = BigCfg::BM;
 using CombineCfg = TileCfg<64, 128, 2, 2>;
-static_assert(SmallCfg::BN == LargeCfg::BN, "both paths cut columns alike");
+static_assert(SmallCfg::BN == LargeCfg::BN && BigCfg::BN == LargeCfg::BN,
+              "all paths cut columns alike");
 
-int ffn_tile_rows(int T, int E, int K)
+int ffn_tile_rows(int T, int E, int K, int int4)
 {
     // rows per expert on average decides the tile height
     const long R = (long)T * K;
-    return (R <= 24L * E) ? SmallCfg::BM : LargeCfg::BM;
+    if (R <= 24L * E) return SmallCfg::BM;
+    return int4 ? LargeCfg::BM : BIG_BM;
 }
 
 long ffn_max_tiles(int T, int E, int K, int bm)
@@ -591,6 +712,23 @@ static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     launch_combine(a, mk, st);
 }
 
+static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
+{
+    const long mt = ffn_max_tiles(a.T, a.E, a.K, BigCfg::BM);
+    const long grid_gu = ((mt * ffn_col_tiles_gu(a.F) + 7) / 8) * 8;
+    const long grid_dn = ((mt * ffn_col_tiles_dn(a.D) + 7) / 8) * 8;
+    mk.mark(st);
+    gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
+        (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.list_gu,
+        a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+    mk.mark(st);
+    down_big_kernel<<<(unsigned)grid_dn, BigCfg::NT, 0, st>>>(
+        (const uint16_t *)a.h, (const uint16_t *)a.down, a.count, a.offset, a.list_dn, a.n_items, a.D,
+        a.F, (uint16_t *)a.o);
+    launch_combine(a, mk, st);
+}
+
 template <class C>
 static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
@@ -627,7 +765,7 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
         } else if (a.bm == SmallCfg::BM) {
             launch_staged<SmallCfg>(a, mk, st);
         } else {
-            launch_staged<LargeCfg>(a, mk, st);
+            launch_big(a, mk, st);
         }
     } else {
         const int64_t n1 = (int64_t)(R + T) * F, n2 = (int64_t)R * D, n3 = (int64_t)T * D;

@@ -62,7 +62,7 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st);
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st);
 
 int perm_tiles(int T);
-int ffn_tile_rows(int T, int E, int K);
+int ffn_tile_rows(int T, int E, int K, int int4);
 long ffn_max_tiles(int T, int E, int K, int bm);
 int ffn_col_tiles_gu(int F);
 int ffn_col_tiles_dn(int D);
