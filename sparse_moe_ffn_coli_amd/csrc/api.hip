@@ -37,7 +37,7 @@ struct RouteWs {
     size_t z, tile_count, tile_base, total;
 };
 struct FfnWs {
-    size_t h, o, list_gu, list_dn, n_items, total;
+    size_t h, o, sx, list_gu, list_dn, n_items, total;
     int bm;
 };
 
@@ -63,7 +63,8 @@ FfnWs ffn_ws(const coli_moe_shape *s, int quant)
     const size_t max_tiles = (size_t)coli::ffn_max_tiles(s->T, s->E, s->K, w.bm);
     w.h = 0;
     w.o = align_up(w.h + (R + T) * F * elt);
-    w.list_gu = align_up(w.o + R * D * elt);
+    w.sx = align_up(w.o + R * D * elt);
+    w.list_gu = align_up(w.sx + T * D * 4);
     w.list_dn = align_up(w.list_gu + max_tiles * (size_t)coli::ffn_col_tiles_gu(s->F) * 16);
     w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * 16);
     w.total = align_up(w.n_items + 16);
@@ -228,6 +229,7 @@ coli_status coli_moe_ffn_timed(const coli_moe_shape *s, const void *x, const col
     a.residual = residual; a.y = y; a.y_bf16 = y_bf16;
     char *base = (char *)ws;
     a.h = base + L.h; a.o = base + L.o;
+    a.sx = (float *)(base + L.sx);
     a.list_gu = (int4 *)(base + L.list_gu);
     a.list_dn = (int4 *)(base + L.list_dn);
     a.n_items = (int32_t *)(base + L.n_items);
@@ -282,6 +284,7 @@ coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
     a.residual = residual; a.y = y; a.y_bf16 = y_bf16;
     char *base = (char *)ws;
     a.h = base + L.h; a.o = base + L.o;
+    a.sx = (float *)(base + L.sx);
     a.list_gu = (int4 *)(base + L.list_gu);
     a.list_dn = (int4 *)(base + L.list_dn);
     a.n_items = (int32_t *)(base + L.n_items);

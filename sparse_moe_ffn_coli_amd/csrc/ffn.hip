@@ -9,15 +9,16 @@
 // the selected experts, clamped SwiGLU between them, the shared expert
 // computed alongside and combined with the weighted routed outputs).
 //
-// bf16 path: three grouped MFMA GEMMs over a device-built list of
+// bf16 path: two grouped MFMA GEMMs over a device-built list of
 // (expert, first row) tiles -- no host synchronisation is needed to learn the
-// per-expert row counts:
+// per-expert row counts -- and an elementwise combine:
 //   1. gate+up over the routed rows AND the shared expert (as expert E with
 //      all T tokens), clamped SwiGLU in the epilogue, h in bf16;
-//   2. down over the routed rows, o in bf16;
-//   3. shared down over the T tokens, whose epilogue adds the routed rows of
-//      each token with one fixed fmaf chain (no atomics: bitwise repeatable).
-// fp32 path: the same three steps with one thread per output value.
+//   2. down over the same rows: routed rows to o in bf16, the shared
+//      expert's rows to sx in fp32;
+//   3. per token and column, sx plus the routed rows of the token in one
+//      fixed fmaf chain (no atomics: bitwise repeatable), plus the residual.
+// fp32 path: the same steps with one thread per output value.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -28,15 +29,15 @@ namespace coli {
 // and, per GEMM, into n_nt column tiles; one entry {expert, first row,
 // column tile} per workgroup.  Within an expert the row tiles are taken in
 // blocks of ROW_BLOCK, and a block's entries are ordered column-tile major,
-// row-tile minor: a block (ROW_BLOCK x n_nt entries) is dispatched together
-// behind one L2 (see xcd_tile), so each weight tile is streamed once per
-// block and shared by its row tiles, and each block of token rows is
-// fetched once and shared by all column tiles.  The gate+up list ends with
-// the shared expert (expert index E over all T tokens); the down list holds
-// the routed experts only.
+// row-tile minor: a block (ROW_BLOCK x n_nt entries) runs together behind one
+// L2 (see xcd_tile), so each weight tile is streamed once per block and
+// shared by its row tiles, and each block of token rows is fetched once and
+// shared by all column tiles.  Both lists hold the routed experts in index
+// order followed by the shared expert (index E, all T tokens).
 // n_items[0] = entries of the down list, n_items[1] = entries of the gate+up list.
 // ---------------------------------------------------------------------------
 constexpr int ROW_BLOCK = 8;
+constexpr int TILE_N = 256;          // columns of a tile in every bf16/int4 grouped kernel
 
 // Entry `local` of an expert with `mte` row tiles and `nnt` column tiles ->
 // (row tile, column tile) in the block order described above.
@@ -54,45 +55,43 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
                                                          int4 *__restrict__ list_dn,
                                                          int32_t *__restrict__ n_items)
 {
-    // sc[e] = row tiles of experts 0..e (inclusive scan); expert E (the
-    // shared one) has ceil(T/BM) row tiles and exists only in the gate+up list
-    __shared__ int32_t sc[1025];
+    // sc[e] = row tiles of routed experts 0..e (inclusive scan); the shared
+    // expert's ceil(T/BM) row tiles follow them
+    __shared__ int32_t sc[1024];
     const int tid = threadIdx.x;
-    const int mt = (tid < E) ? (count[tid] + BM - 1) / BM : 0;
-    sc[tid] = mt;
+    sc[tid] = (tid < E) ? (count[tid] + BM - 1) / BM : 0;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-        int v = (tid >= off) ? sc[tid - off] : 0;
+        const int v = (tid >= off) ? sc[tid - off] : 0;
         __syncthreads();
         sc[tid] += v;
         __syncthreads();
     }
     const int routed = sc[1023];
     const int mt_sh = (T + BM - 1) / BM;
-    if (tid == 0) sc[1024] = routed + mt_sh;
-    __syncthreads();
-    // expert owning row tile index i: the first e with sc[e] > i
-    auto owner = [&](int i, int last) {
-        int lo = 0, hi = last;
+    // expert owning row tile index i < routed: the first e with sc[e] > i
+    auto owner = [&](int i) {
+        int lo = 0, hi = E - 1;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
             if (sc[mid] > i) hi = mid; else lo = mid + 1;
         }
         return lo;
     };
-    const int n_gu = (routed + mt_sh) * nnt_gu, n_dn = routed * nnt_dn;
-    // entry index q -> (expert, column tile, row tile), column-major inside an expert
+    const int n_gu = (routed + mt_sh) * nnt_gu, n_dn = (routed + mt_sh) * nnt_dn;
     for (int q = tid; q < n_gu; q += 1024) {
-        const int e = (q < routed * nnt_gu) ? owner(q / nnt_gu, E - 1) : E;
+        const int i = q / nnt_gu;
+        const int e = (i < routed) ? owner(i) : E;
         const int mte = (e == E) ? mt_sh : (count[e] + BM - 1) / BM;
         const int first = (e == E) ? routed : sc[e] - mte;
         const int2 mn = block_order(q - first * nnt_gu, mte, nnt_gu);
         list_gu[q] = make_int4(e, mn.x * BM, mn.y, 0);
     }
     for (int q = tid; q < n_dn; q += 1024) {
-        const int e = owner(q / nnt_dn, E - 1);
-        const int mte = (count[e] + BM - 1) / BM;
-        const int first = sc[e] - mte;
+        const int i = q / nnt_dn;
+        const int e = (i < routed) ? owner(i) : E;
+        const int mte = (e == E) ? mt_sh : (count[e] + BM - 1) / BM;
+        const int first = (e == E) ? routed : sc[e] - mte;
         const int2 mn = block_order(q - first * nnt_dn, mte, nnt_dn);
         list_dn[q] = make_int4(e, mn.x * BM, mn.y, 0);
     }
@@ -135,12 +134,12 @@ __device__ __forceinline__ const uint16_t *gateup_b_row(const uint16_t *G, const
 }
 
 // XCD-aware block -> tile map.  Workgroups are dispatched to the 8 XCDs
-// round-robin (block b runs on XCD b % 8).  The actual tile count (known only
-// on the device) is split into 8 contiguous ranges, and the blocks of XCD x
-// take the tiles of range x in order, so tiles that share A rows (same rows,
-// neighbouring columns) or B rows (same expert and columns, neighbouring
-// rows) run at the same time behind the same L2.  The grid is an upper bound;
-// surplus blocks return -1.
+// round-robin (block b runs on XCD b % 8, the blocks of one XCD in order).
+// The actual tile count (known only on the device) is split into 8
+// contiguous ranges, and the blocks of XCD x take the tiles of range x in
+// order, so tiles that share A rows (same rows, neighbouring columns) or B
+// rows (same expert and columns, neighbouring rows) run at the same time
+// behind the same L2.  The grid is an upper bound; surplus blocks return -1.
 __device__ __forceinline__ int xcd_tile(int ntiles)
 {
     const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
@@ -148,6 +147,8 @@ __device__ __forceinline__ int xcd_tile(int ntiles)
     const int t = x * per + w;
     return (w < per && t < ntiles) ? t : -1;
 }
+
+static long xcd_grid(long max_items) { return ((max_items + 7) / 8) * 8; }
 
 // ---------------------------------------------------------------------------
 // 1. gate+up grouped GEMM with the clamped SwiGLU in the epilogue, h in bf16.
@@ -207,37 +208,44 @@ __global__ __launch_bounds__(256) void gateup_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 2. down grouped GEMM over the routed rows: o[row] = W_down[e] h[row], o in bf16.
+// 2. down grouped GEMM: o[row] = W_down[e] h[row] in bf16 for the routed rows,
+//    sx[t] = S_down h[R + t] in fp32 for the shared expert's rows.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_down(const ExpertTile &et, int r, int d, int D, float v,
+                                           uint16_t *__restrict__ o, float *__restrict__ sx)
+{
+    if (et.shared) sx[(size_t)r * D + d] = v;
+    else o[(size_t)(et.base + r) * D + d] = f32_to_bf16_bits(v);
+}
+
 template <class C>
 __global__ __launch_bounds__(256) void down_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ down,
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int F,
-    uint16_t *__restrict__ o)
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int K, int F,
+    uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
     const int t = xcd_tile(n_items[0]);
     if (t < 0) return;
     const int4 item = list[t];
-    const int e = item.x, m0 = item.y, nt = item.z;   // the last column tile may be ragged
-    const int cnt = count[e];
-    const int base = offset[e];
-    const int d0 = nt * C::BN;
+    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
+    const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
+    const int d0 = item.z * C::BN;                    // the last column tile may be ragged
     const int ch0 = threadIdx.x & 7;
 
     const uint16_t *ap[C::A_PER_T];
     const uint16_t *bp[C::B_PER_T];
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i) {
-        int rr = a_chunk_row<C>(i);
-        int r = (rr < C::BM && m0 + rr < cnt) ? m0 + rr : m0;
-        ap[i] = h + (size_t)(base + r) * F + ch0 * 8;
+        const int rr = a_chunk_row<C>(i);
+        const int r = (rr < C::BM && et.m0 + rr < et.cnt) ? et.m0 + rr : et.m0;
+        ap[i] = h + (size_t)(et.base + r) * F + ch0 * 8;
     }
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i) {
-        int d = min(d0 + a_chunk_row<C>(i), D - 1);    // rows past D reread the last one
-        bp[i] = down + ((size_t)e * D + d) * F + ch0 * 8;
+        const int d = min(d0 + a_chunk_row<C>(i), D - 1);    // rows past D reread the last one
+        bp[i] = W + (size_t)d * F + ch0 * 8;
     }
     f32x16 acc[C::FM][C::FN];
     mfma_mainloop<C>(ap, bp, F, lds, acc);
@@ -251,8 +259,8 @@ __global__ __launch_bounds__(256) void down_kernel(
             const int d = d0 + acc_col<C>(wn, n, lane);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int r = m0 + acc_row<C>(wm, m, lane, i);
-                if (r < cnt && d < D) o[(size_t)(base + r) * D + d] = f32_to_bf16_bits(acc[m][n][i]);
+                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
+                if (r < et.cnt && d < D) store_down(et, r, d, D, acc[m][n][i], o, sx);
             }
         }
 }
@@ -323,12 +331,12 @@ __global__ __launch_bounds__(512) void gateup_big_kernel(
 }
 
 template <int NFW>
-__device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg::CPW], int m0, int cnt,
-                                              int base, int d0, int D, int F, int w, char *lds,
-                                              uint16_t *__restrict__ o)
+__device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg::CPW], const ExpertTile &et,
+                                              int d0, int D, int F, int w, char *lds,
+                                              uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     f32x16 acc[BigCfg::FM][BigCfg::FN];
-    big_mainloop<BigCfg, NFW>(rp, F, min(cnt - m0, BigCfg::BM), w, lds, acc);
+    big_mainloop<BigCfg, NFW>(rp, F, min(et.cnt - et.m0, BigCfg::BM), w, lds, acc);
     const int lane = threadIdx.x & 63, wm = w >> 1, wn = w & 1;
 #pragma unroll
     for (int m = 0; m < NFW; ++m)
@@ -337,42 +345,41 @@ __device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg
             const int d = d0 + (wn * BigCfg::FN + n) * 32 + (lane & 31);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int r = m0 + wm * 64 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (r < cnt && d < D) o[(size_t)(base + r) * D + d] = f32_to_bf16_bits(acc[m][n][i]);
+                const int r = et.m0 + wm * 64 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (r < et.cnt && d < D) store_down(et, r, d, D, acc[m][n][i], o, sx);
             }
         }
 }
 
 __global__ __launch_bounds__(512) void down_big_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ down,
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int F,
-    uint16_t *__restrict__ o)
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int K, int F,
+    uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(1024))) char lds[BigCfg::LDS_BYTES];
     const int t = xcd_tile(n_items[0]);
     if (t < 0) return;
     const int4 item = list[t];
-    const int e = item.x, m0 = item.y;
-    const int cnt = count[e], base = offset[e];
+    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
     const int d0 = item.z * BigCfg::BN;
-    const uint16_t *W = down + (size_t)e * D * F;
+    const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint16_t *rp[BigCfg::CPW];
 #pragma unroll
     for (int j = 0; j < BigCfg::CPO; ++j) {
         const int row = big_copy_row<BigCfg>(j, w);
         const int ch = big_copy_chunk<BigCfg>(row);
-        int r = m0 + row;
-        if (r >= cnt) r = m0;
-        rp[j] = h + (size_t)(base + r) * F + ch * 8;
+        int r = et.m0 + row;
+        if (r >= et.cnt) r = et.m0;
+        rp[j] = h + (size_t)(et.base + r) * F + ch * 8;
         const int d = min(d0 + row, D - 1);       // rows past D reread the last one
         rp[BigCfg::CPO + j] = W + (size_t)d * F + ch * 8;
     }
-    const int nfw = big_wave_fragments(cnt - m0, w >> 1);
-    if (nfw == 2) down_big_body<2>(rp, m0, cnt, base, d0, D, F, w, lds, o);
-    else if (nfw == 1) down_big_body<1>(rp, m0, cnt, base, d0, D, F, w, lds, o);
-    else down_big_body<0>(rp, m0, cnt, base, d0, D, F, w, lds, o);
+    const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
+    if (nfw == 2) down_big_body<2>(rp, et, d0, D, F, w, lds, o, sx);
+    else if (nfw == 1) down_big_body<1>(rp, et, d0, D, F, w, lds, o, sx);
+    else down_big_body<0>(rp, et, d0, D, F, w, lds, o, sx);
 }
 
 // ---------------------------------------------------------------------------
@@ -445,32 +452,35 @@ __global__ __launch_bounds__(256) void gateup_int4_kernel(
 template <class C>
 __global__ __launch_bounds__(256) void down_int4_kernel(
     const uint16_t *__restrict__ h, const uint8_t *__restrict__ down_q, const uint16_t *__restrict__ down_s,
-    int group, const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int F,
-    uint16_t *__restrict__ o)
+    int group, const uint16_t *__restrict__ s_down, const int32_t *__restrict__ count,
+    const int32_t *__restrict__ offset, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
+    int T, int D, int E, int K, int F, uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
     const int t = xcd_tile(n_items[0]);
     if (t < 0) return;
     const int4 item = list[t];
-    const int e = item.x, m0 = item.y, nt = item.z;
-    const int cnt = count[e];
-    const int base = offset[e];
-    const int d0 = nt * C::BN;
+    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
+    const int d0 = item.z * C::BN;
     const int ch0 = threadIdx.x & 7;
 
     const uint16_t *ap[C::A_PER_T];
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i) {
-        int rr = a_chunk_row<C>(i);
-        int r = (rr < C::BM && m0 + rr < cnt) ? m0 + rr : m0;
-        ap[i] = h + (size_t)(base + r) * F + ch0 * 8;
+        const int rr = a_chunk_row<C>(i);
+        const int r = (rr < C::BM && et.m0 + rr < et.cnt) ? et.m0 + rr : et.m0;
+        ap[i] = h + (size_t)(et.base + r) * F + ch0 * 8;
     }
+    // this thread's B row: the shared expert's dense bf16 row, else int4
     const int d = min(d0 + (int)threadIdx.x, D - 1);
-    const size_t row = (size_t)e * D + d;
     f32x16 acc[C::FM][C::FN];
-    mfma_mainloop_f16<C>(ap, nullptr, down_q + row * (F / 2), down_s + row * (F / group), group, F, lds,
-                         acc);
+    if (et.shared) {
+        mfma_mainloop_f16<C>(ap, s_down + (size_t)d * F, nullptr, nullptr, group, F, lds, acc);
+    } else {
+        const size_t row = (size_t)et.e * D + d;
+        mfma_mainloop_f16<C>(ap, nullptr, down_q + row * (F / 2), down_s + row * (F / group), group, F, lds,
+                             acc);
+    }
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
@@ -481,110 +491,66 @@ __global__ __launch_bounds__(256) void down_int4_kernel(
             const int dd = d0 + acc_col<C>(wn, n, lane);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int r = m0 + acc_row<C>(wm, m, lane, i);
-                if (r < cnt && dd < D) o[(size_t)(base + r) * D + dd] = f32_to_bf16_bits(acc[m][n][i]);
+                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
+                if (r < et.cnt && dd < D) store_down(et, r, dd, D, acc[m][n][i], o, sx);
             }
         }
 }
 
 // ---------------------------------------------------------------------------
-// 3. shared down GEMM over the tokens with the combine in the epilogue:
-//    v = S(x_t)[d]; v = fmaf(w_tj, o[inv(t,j)][d], v) for j = 0..K-1;
-//    y = residual + v.
-// The GEMM result is staged through LDS so that each thread then owns 8
-// consecutive columns of one token and reads the routed rows of o with
-// 16-byte loads.
+// 3. combine: per token t and column d,
+//      v = sx[t][d]; v = fmaf(w_tj, o[inv(t,j)][d], v) for j = 0..K-1;
+//      y = residual + v
+//    Each thread owns 8 consecutive columns of one token (16-byte loads of
+//    the routed rows); every routed row of the token is fetched before the
+//    fixed-order sum.
 // ---------------------------------------------------------------------------
-template <class C>
-__global__ __launch_bounds__(256) void combine_bf16_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ s_down, const uint16_t *__restrict__ o,
-    const float *__restrict__ w, const int32_t *__restrict__ inv, const float *residual, int T, int D,
-    int K, int F, float *y, uint16_t *__restrict__ y_bf16)
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ sx, const uint16_t *__restrict__ o,
+                                                      const float *__restrict__ w, const int32_t *__restrict__ inv,
+                                                      const float *residual, int T, int D, int K, float *y,
+                                                      uint16_t *__restrict__ y_bf16)
 {
-    static_assert(C::BM * C::BN * 4 <= C::LDS_BYTES, "epilogue staging fits the tile's LDS");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const int n_nt = (D + C::BN - 1) / C::BN;
-    const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
-    const int t0 = mt * C::BM, d0 = nt * C::BN;
-    const int R = T * K;
-    const int ch0 = threadIdx.x & 7;
-
-    const uint16_t *ap[C::A_PER_T];
-    const uint16_t *bp[C::B_PER_T];
+    const int per_row = D / 8;
+    const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= (long)T * per_row) return;
+    const int t = (int)(q / per_row), d = (int)(q % per_row) * 8;
+    float wj[8];
+    u32x4 ov[8];
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-        int rr = a_chunk_row<C>(i);
-        int t = (rr < C::BM && t0 + rr < T) ? t0 + rr : t0;
-        ap[i] = h + (size_t)(R + t) * F + ch0 * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-        int d = min(d0 + a_chunk_row<C>(i), D - 1);
-        bp[i] = s_down + (size_t)d * F + ch0 * 8;
-    }
-    f32x16 acc[C::FM][C::FN];
-    mfma_mainloop<C>(ap, bp, F, lds, acc);
-
-    // stage S(x) for the tile: sx[row][col] fp32, once every wave is done
-    // reading the mainloop's last stage
-    __syncthreads();
-    float *sx = reinterpret_cast<float *>(lds);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
-#pragma unroll
-    for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-        for (int n = 0; n < C::FN; ++n) {
-            const int c = acc_col<C>(wn, n, lane);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sx[acc_row<C>(wm, m, lane, i) * C::BN + c] = acc[m][n][i];
+    for (int j = 0; j < 8; ++j)
+        if (j < K) {
+            wj[j] = w[(size_t)t * K + j];
+            ov[j] = *reinterpret_cast<const u32x4 *>(o + (size_t)inv[(size_t)t * K + j] * D + d);
         }
-    __syncthreads();
-
-    constexpr int CHUNKS = C::BM * C::BN / 8;
-    for (int q = threadIdx.x; q < CHUNKS; q += C::NT) {
-        const int row = q / (C::BN / 8), c8 = (q % (C::BN / 8)) * 8;
-        const int t = t0 + row, d = d0 + c8;
-        if (t >= T || d >= D) continue;
-        // all routed rows of the token are fetched before the fixed-order sum
-        float wj[8];
-        u32x4 ov[8];
+    const size_t idx = (size_t)t * D + d;
+    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sx + idx);
+    const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sx + idx + 4);
+    float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < K) {
-                wj[j] = w[(size_t)t * K + j];
-                ov[j] = *reinterpret_cast<const u32x4 *>(o + (size_t)inv[(size_t)t * K + j] * D + d);
-            }
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = sx[row * C::BN + c8 + k];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < K)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    v[2 * k] = fmaf(wj[j], __uint_as_float(ov[j][k] << 16), v[2 * k]);
-                    v[2 * k + 1] = fmaf(wj[j], __uint_as_float(ov[j][k] & 0xffff0000u), v[2 * k + 1]);
-                }
-        const size_t idx = (size_t)t * D + d;
-        if (residual) {
-            const f32x4 r0 = *reinterpret_cast<const f32x4 *>(residual + idx);
-            const f32x4 r1 = *reinterpret_cast<const f32x4 *>(residual + idx + 4);
+    for (int j = 0; j < 8; ++j)
+        if (j < K)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                v[k] = r0[k] + v[k];
-                v[4 + k] = r1[k] + v[4 + k];
+                v[2 * k] = fmaf(wj[j], __uint_as_float(ov[j][k] << 16), v[2 * k]);
+                v[2 * k + 1] = fmaf(wj[j], __uint_as_float(ov[j][k] & 0xffff0000u), v[2 * k + 1]);
             }
-        }
-        *reinterpret_cast<f32x4 *>(y + idx) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4 *>(y + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
-        if (y_bf16) {
-            u32x4 pk;
+    if (residual) {
+        const f32x4 r0 = *reinterpret_cast<const f32x4 *>(residual + idx);
+        const f32x4 r1 = *reinterpret_cast<const f32x4 *>(residual + idx + 4);
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                pk[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
-            *reinterpret_cast<u32x4 *>(y_bf16 + idx) = pk;
+        for (int k = 0; k < 4; ++k) {
+            v[k] = r0[k] + v[k];
+            v[4 + k] = r1[k] + v[4 + k];
         }
+    }
+    *reinterpret_cast<f32x4 *>(y + idx) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(y + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    if (y_bf16) {
+        u32x4 pk;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            pk[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
+        *reinterpret_cast<u32x4 *>(y_bf16 + idx) = pk;
     }
 }
 
@@ -660,8 +626,7 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 using SmallCfg = TileCfg<32, 256, 1, 4>;
 using LargeCfg = TileCfg<64, 256, 2, 2>;
 constexpr int BIG_BM = BigCfg::BM;
-using CombineCfg = TileCfg<64, 128, 2, 2>;
-static_assert(SmallCfg::BN == LargeCfg::BN && BigCfg::BN == LargeCfg::BN,
+static_assert(SmallCfg::BN == TILE_N && LargeCfg::BN == TILE_N && BigCfg::BN == TILE_N,
               "all paths cut columns alike");
 
 int ffn_tile_rows(int T, int E, int K, int int4)
@@ -678,28 +643,24 @@ long ffn_max_tiles(int T, int E, int K, int bm)
     return R / bm + (R < E ? R : E) + (T + bm - 1) / bm;
 }
 
-int ffn_col_tiles_gu(int F) { return (F + LargeCfg::BN / 2 - 1) / (LargeCfg::BN / 2); }
-int ffn_col_tiles_dn(int D) { return (D + LargeCfg::BN - 1) / LargeCfg::BN; }
+int ffn_col_tiles_gu(int F) { return (F + TILE_N / 2 - 1) / (TILE_N / 2); }
+int ffn_col_tiles_dn(int D) { return (D + TILE_N - 1) / TILE_N; }
 
 static void launch_combine(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
-    using C = CombineCfg;
-    const int n_nt_d = (a.D + C::BN - 1) / C::BN;
-    const int n_mt = (a.T + C::BM - 1) / C::BM;
+    const long n = (long)a.T * (a.D / 8);
     mk.mark(st);
-    combine_bf16_kernel<C><<<(unsigned)(n_mt * n_nt_d), 256, 0, st>>>(
-        (const uint16_t *)a.h, (const uint16_t *)a.s_down, (const uint16_t *)a.o, a.w, a.inv,
-        a.residual, a.T, a.D, a.K, a.F, a.y, (uint16_t *)a.y_bf16);
+    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
+        a.sx, (const uint16_t *)a.o, a.w, a.inv, a.residual, a.T, a.D, a.K, a.y, (uint16_t *)a.y_bf16);
     mk.mark(st);
 }
 
 template <class C>
 static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
-    // grids are upper bounds of the list lengths (rounded to whole XCD groups)
     const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
-    const long grid_gu = ((mt * ffn_col_tiles_gu(a.F) + 7) / 8) * 8;
-    const long grid_dn = ((mt * ffn_col_tiles_dn(a.D) + 7) / 8) * 8;
+    const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
+    const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     mk.mark(st);
     gateup_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
@@ -707,16 +668,16 @@ static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
         a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
-        (const uint16_t *)a.h, (const uint16_t *)a.down, a.count, a.offset, a.list_dn, a.n_items, a.D,
-        a.F, (uint16_t *)a.o);
+        (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count, a.offset,
+        a.list_dn, a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 
 static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
     const long mt = ffn_max_tiles(a.T, a.E, a.K, BigCfg::BM);
-    const long grid_gu = ((mt * ffn_col_tiles_gu(a.F) + 7) / 8) * 8;
-    const long grid_dn = ((mt * ffn_col_tiles_dn(a.D) + 7) / 8) * 8;
+    const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
+    const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     mk.mark(st);
     gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
@@ -724,8 +685,8 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
         a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_big_kernel<<<(unsigned)grid_dn, BigCfg::NT, 0, st>>>(
-        (const uint16_t *)a.h, (const uint16_t *)a.down, a.count, a.offset, a.list_dn, a.n_items, a.D,
-        a.F, (uint16_t *)a.o);
+        (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count, a.offset,
+        a.list_dn, a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 
@@ -733,8 +694,8 @@ template <class C>
 static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
     const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
-    const long grid_gu = ((mt * ffn_col_tiles_gu(a.F) + 7) / 8) * 8;
-    const long grid_dn = ((mt * ffn_col_tiles_dn(a.D) + 7) / 8) * 8;
+    const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
+    const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     mk.mark(st);
     gateup_int4_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         (const uint16_t *)a.x, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
@@ -742,8 +703,8 @@ static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t s
         a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_int4_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
-        (const uint16_t *)a.h, a.down_q, a.down_s, a.group, a.count, a.offset, a.list_dn, a.n_items,
-        a.D, a.F, (uint16_t *)a.o);
+        (const uint16_t *)a.h, a.down_q, a.down_s, a.group, (const uint16_t *)a.s_down, a.count, a.offset,
+        a.list_dn, a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 

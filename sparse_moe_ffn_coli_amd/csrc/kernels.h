@@ -52,6 +52,7 @@ struct FfnLaunch {
     void *y_bf16;
     void *h;               // workspace [T*K + T][F]
     void *o;               // workspace [T*K][D]
+    float *sx;             // workspace [T][D] (bf16 path): the shared expert's output
     int4 *list_gu;         // workspace [ffn_max_tiles * ffn_col_tiles_gu]
     int4 *list_dn;         // workspace [ffn_max_tiles * ffn_col_tiles_dn]
     int32_t *n_items;      // workspace [2]
