@@ -122,7 +122,8 @@ typedef struct {
 } coli_moe_weights_int4;
 
 /* Bytes of workspace an entry point needs for this shape (int4 != 0 for the
- * int4 FFN).  The same workspace may serve route and FFN calls of the shape. */
+ * int4 FFN); at least 256, and 0 for an invalid shape.  The same workspace
+ * may serve route and FFN calls of the shape. */
 size_t coli_moe_workspace_bytes(const coli_moe_shape *s, int int4);
 
 /* Router, top-K selection, weight normalisation and the stable permutation
@@ -156,9 +157,9 @@ coli_status coli_moe_ffn_int4(const coli_moe_shape *s, const void *x,
  * `stream`: events[i] just before stage i is enqueued and events[n_stages]
  * after the last one.  Entries past n_events, and NULL entries, are skipped.
  * Nothing is recorded when the call fails validation or T = 0.
- *   route stages (5): router logits, top-K, tile histogram, scan, scatter
- *   ffn stages (4):   tile list, gate+up (+SwiGLU), down, shared down + combine
- *                     (the fp32 path has no tile list: events 0 and 1 coincide) */
+ *   route stages (3): router logits, top-K, permutation
+ *   ffn stages (3):   gate+up (+SwiGLU; for large batches also the kernel
+ *                     that lists the tiles), down (routed and shared), combine */
 coli_status coli_moe_route_timed(const coli_moe_shape *s, const void *x, const void *w_router,
                                  const float *bias, const coli_moe_routing *out, void *ws,
                                  size_t ws_bytes, void *stream, void *const *events,

@@ -34,8 +34,8 @@ STATUS_NAMES = {0: "COLI_OK", 1: "COLI_E_NULL", 2: "COLI_E_SHAPE", 3: "COLI_E_DT
 EXPORTED = ("coli_moe_workspace_bytes", "coli_moe_route", "coli_moe_ffn", "coli_moe_ffn_int4",
             "coli_moe_route_timed", "coli_moe_ffn_timed", "coli_moe_ffn_int4_timed",
             "coli_moe_status_str", "coli_moe_version")
-ROUTE_STAGES = ("router", "topk", "perm_hist", "perm_scan", "perm_scatter")
-FFN_STAGES = ("tiles", "gate_up", "down", "combine")
+ROUTE_STAGES = ("router", "topk", "perm")
+FFN_STAGES = ("gate_up", "down", "combine")
 
 
 class ColiError(RuntimeError):

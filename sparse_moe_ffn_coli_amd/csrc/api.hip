@@ -47,7 +47,7 @@ RouteWs route_ws(const coli_moe_shape *s)
     const size_t T = (size_t)s->T, E = (size_t)s->E;
     const size_t ntiles = (size_t)coli::perm_tiles(s->T);
     w.z = 0;
-    w.tile_count = align_up(w.z + T * E * 4);
+    w.tile_count = align_up(w.z + (size_t)coli::router_splits(s->T, s->D) * T * E * 4);
     w.tile_base = align_up(w.tile_count + ntiles * E * 4);
     w.total = align_up(w.tile_base + ntiles * E * 4);
     return w;
@@ -60,10 +60,10 @@ FfnWs ffn_ws(const coli_moe_shape *s, int quant)
     const size_t R = T * K;
     const size_t elt = (s->dtype == COLI_F32) ? 4 : 2;
     w.bm = coli::ffn_tile_rows(s->T, s->E, s->K, quant);
-    const size_t max_tiles = (size_t)coli::ffn_max_tiles(s->T, s->E, s->K, w.bm);
     w.h = 0;
     w.o = align_up(w.h + (R + T) * F * elt);
     w.sx = align_up(w.o + R * D * elt);
+    const size_t max_tiles = (size_t)coli::ffn_max_tiles(s->T, s->E, s->K, w.bm);
     w.list_gu = align_up(w.sx + T * D * 4);
     w.list_dn = align_up(w.list_gu + max_tiles * (size_t)coli::ffn_col_tiles_gu(s->F) * 16);
     w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * 16);
@@ -132,7 +132,8 @@ size_t coli_moe_workspace_bytes(const coli_moe_shape *s, int int4)
 {
     if (check_shape(s) != COLI_OK) return 0;
     const size_t a = route_ws(s).total, b = ffn_ws(s, int4).total;
-    return a > b ? a : b;
+    const size_t n = a > b ? a : b;
+    return n > 256 ? n : 256;       // never 0, which reports an invalid shape
 }
 
 coli_status coli_moe_route(const coli_moe_shape *s, const void *x, const void *w_router,

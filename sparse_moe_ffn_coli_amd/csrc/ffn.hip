@@ -25,21 +25,27 @@
 namespace coli {
 
 // ---------------------------------------------------------------------------
-// Work lists.  Every expert with rows is cut into ceil(count/BM) row tiles
-// and, per GEMM, into n_nt column tiles; one entry {expert, first row,
-// column tile} per workgroup.  Within an expert the row tiles are taken in
-// blocks of ROW_BLOCK, and a block's entries are ordered column-tile major,
-// row-tile minor: a block (ROW_BLOCK x n_nt entries) runs together behind one
-// L2 (see xcd_tile), so each weight tile is streamed once per block and
-// shared by its row tiles, and each block of token rows is fetched once and
-// shared by all column tiles.  Both lists hold the routed experts in index
-// order followed by the shared expert (index E, all T tokens).
-// n_items[0] = entries of the down list, n_items[1] = entries of the gate+up list.
+// Tile order.  Every expert with rows is cut into ceil(count/BM) row tiles
+// and, per GEMM, into n_nt column tiles: one workgroup per (expert, row tile,
+// column tile).  The tiles are numbered expert by expert (routed experts in
+// index order, then the shared expert: index E, all T tokens).  Within an
+// expert the row tiles are taken in blocks of ROW_BLOCK, and a block's tiles
+// are numbered column-tile major, row-tile minor: a block (ROW_BLOCK x n_nt
+// tiles) runs together behind one L2 (see xcd_tile), so each weight tile is
+// streamed once per block and shared by its row tiles, and each block of
+// token rows is fetched once and shared by all column tiles.
+//
+// Each workgroup finds its own tile from the per-expert row counts (no list
+// in memory, no extra launch): every wave scans the counts itself -- lane l
+// sums the row tiles of a contiguous run of experts, a wave-wide inclusive
+// scan of those sums locates the lane whose run holds the tile, and that
+// run is walked -- with shuffles and a ballot only, so no LDS and no
+// barrier.  All waves reach the same answer.
 // ---------------------------------------------------------------------------
 constexpr int ROW_BLOCK = 8;
 constexpr int TILE_N = 256;          // columns of a tile in every bf16/int4 grouped kernel
 
-// Entry `local` of an expert with `mte` row tiles and `nnt` column tiles ->
+// Tile `local` of an expert with `mte` row tiles and `nnt` column tiles ->
 // (row tile, column tile) in the block order described above.
 __device__ __forceinline__ int2 block_order(int local, int mte, int nnt)
 {
@@ -49,6 +55,78 @@ __device__ __forceinline__ int2 block_order(int local, int mte, int nnt)
     return make_int2(blk * ROW_BLOCK + in % rows, in / rows);
 }
 
+// XCD-aware block -> tile map.  Workgroups are dispatched to the 8 XCDs
+// round-robin (block b runs on XCD b % 8, the blocks of one XCD in order).
+// The actual tile count (known only on the device) is split into 8
+// contiguous ranges, and the blocks of XCD x take the tiles of range x in
+// order, so tiles that share A rows (same rows, neighbouring columns) or B
+// rows (same expert and columns, neighbouring rows) run at the same time
+// behind the same L2.  The grid is an upper bound; surplus blocks return -1.
+__device__ __forceinline__ int xcd_tile(int ntiles)
+{
+    const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
+    const int per = (ntiles + 7) >> 3;
+    const int t = x * per + w;
+    return (w < per && t < ntiles) ? t : -1;
+}
+
+static long xcd_grid(long max_items) { return ((max_items + 7) / 8) * 8; }
+
+struct WorkTile {
+    int e, m0, ct;          // expert (E: the shared one), first row, column tile; e < 0: no tile
+};
+
+constexpr int FIND_MAX_RUN = 16;     // experts per lane for E <= 1024
+
+__device__ __forceinline__ WorkTile find_tile(const int32_t *__restrict__ count, int E, int T, int BM, int nnt)
+{
+    const int lane = threadIdx.x & 63;
+    const int run = (E + 63) >> 6;                 // experts per lane
+    // all counts are loaded at once; each lane keeps the row tiles of its run
+    int mtk[FIND_MAX_RUN];
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < FIND_MAX_RUN; ++k) {
+        const int e = lane * run + k;
+        mtk[k] = (k < run && e < E) ? (count[e] + BM - 1) / BM : 0;
+        local += mtk[k];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    const int routed = __shfl(incl, 63);
+    const int mt_sh = (T + BM - 1) / BM;
+    const int t = xcd_tile((routed + mt_sh) * nnt);
+    if (t < 0) return WorkTile{-1, 0, 0};
+    const int i = t / nnt;                         // row tile index over all experts
+    int e = E, mte = mt_sh, first = routed;
+    if (i < routed) {
+        const int L = __builtin_ctzll(__ballot(incl > i));   // first lane whose run ends past i
+        first = __shfl(incl - local, L);
+        // walk lane L's run with its register copies (the loop bounds are
+        // uniform, so every lane takes part in each shuffle)
+#pragma unroll
+        for (int k = 0; k < FIND_MAX_RUN; ++k) {
+            const int m = __shfl(mtk[k], L);
+            if (first + m > i) {
+                e = L * run + k;
+                mte = m;
+                break;
+            }
+            first += m;
+        }
+    }
+    const int2 mn = block_order(t - first * nnt, mte, nnt);
+    return WorkTile{e, mn.x * BM, mn.y};
+}
+
+// The 256 x 256 kernels run one workgroup per CU, so nothing hides a
+// per-tile search there: their tiles come from a list built beforehand by
+// one small kernel in the same order (n_items[0] = entries of the down list,
+// n_items[1] = entries of the gate+up list).
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
                                                          int BM, int nnt_gu, int nnt_dn,
                                                          int4 *__restrict__ list_gu,
@@ -109,15 +187,15 @@ struct ExpertTile {
     bool shared;
 };
 
-__device__ __forceinline__ ExpertTile decode_tile(const int4 &tl, const int32_t *count,
+__device__ __forceinline__ ExpertTile decode_tile(const WorkTile &wt, const int32_t *count,
                                                   const int32_t *offset, int E, int T, int R)
 {
     ExpertTile r;
-    r.e = tl.x;
-    r.m0 = tl.y;
-    r.shared = (tl.x == E);
-    r.cnt = r.shared ? T : count[tl.x];
-    r.base = r.shared ? R : offset[tl.x];
+    r.e = wt.e;
+    r.m0 = wt.m0;
+    r.shared = (wt.e == E);
+    r.cnt = r.shared ? T : count[wt.e];
+    r.base = r.shared ? R : offset[wt.e];
     return r;
 }
 
@@ -133,23 +211,6 @@ __device__ __forceinline__ const uint16_t *gateup_b_row(const uint16_t *G, const
     return ((blk & 1) ? U : G) + (size_t)f * D;
 }
 
-// XCD-aware block -> tile map.  Workgroups are dispatched to the 8 XCDs
-// round-robin (block b runs on XCD b % 8, the blocks of one XCD in order).
-// The actual tile count (known only on the device) is split into 8
-// contiguous ranges, and the blocks of XCD x take the tiles of range x in
-// order, so tiles that share A rows (same rows, neighbouring columns) or B
-// rows (same expert and columns, neighbouring rows) run at the same time
-// behind the same L2.  The grid is an upper bound; surplus blocks return -1.
-__device__ __forceinline__ int xcd_tile(int ntiles)
-{
-    const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
-    const int per = (ntiles + 7) >> 3;
-    const int t = x * per + w;
-    return (w < per && t < ntiles) ? t : -1;
-}
-
-static long xcd_grid(long max_items) { return ((max_items + 7) / 8) * 8; }
-
 // ---------------------------------------------------------------------------
 // 1. gate+up grouped GEMM with the clamped SwiGLU in the epilogue, h in bf16.
 // ---------------------------------------------------------------------------
@@ -158,16 +219,14 @@ __global__ __launch_bounds__(256) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
-    int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+    const int32_t *__restrict__ perm, int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
 {
     static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
     constexpr int FC = C::BN / 2;                 // output columns per tile
-    const int t = xcd_tile(n_items[1]);
-    if (t < 0) return;
-    const int4 item = list[t];
-    const int nt = item.z;
+    const WorkTile item = find_tile(count, E, T, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
+    if (item.e < 0) return;
+    const int nt = item.ct;
     const int R = T * K;
     const ExpertTile et = decode_tile(item, count, offset, E, T, R);
     const uint16_t *G = et.shared ? s_gate : gate + (size_t)et.e * F * D;
@@ -222,16 +281,15 @@ template <class C>
 __global__ __launch_bounds__(256) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int K, int F,
+    int T, int D, int E, int K, int F,
     uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const int t = xcd_tile(n_items[0]);
-    if (t < 0) return;
-    const int4 item = list[t];
+    const WorkTile item = find_tile(count, E, T, C::BM, (D + TILE_N - 1) / TILE_N);
+    if (item.e < 0) return;
     const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
-    const int d0 = item.z * C::BN;                    // the last column tile may be ragged
+    const int d0 = item.ct * C::BN;                    // the last column tile may be ragged
     const int ch0 = threadIdx.x & 7;
 
     const uint16_t *ap[C::A_PER_T];
@@ -307,11 +365,12 @@ __global__ __launch_bounds__(512) void gateup_big_kernel(
     __shared__ __attribute__((aligned(1024))) char lds[BigCfg::LDS_BYTES];
     const int t = xcd_tile(n_items[1]);
     if (t < 0) return;
-    const int4 item = list[t];
+    const int4 entry = list[t];
+    const WorkTile item{entry.x, entry.y, entry.z};
     const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
     const uint16_t *G = et.shared ? s_gate : gate + (size_t)et.e * F * D;
     const uint16_t *U = et.shared ? s_up : up + (size_t)et.e * F * D;
-    const int f0 = item.z * (BigCfg::BN / 2);
+    const int f0 = item.ct * (BigCfg::BN / 2);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint16_t *rp[BigCfg::CPW];
 #pragma unroll
@@ -360,9 +419,10 @@ __global__ __launch_bounds__(512) void down_big_kernel(
     __shared__ __attribute__((aligned(1024))) char lds[BigCfg::LDS_BYTES];
     const int t = xcd_tile(n_items[0]);
     if (t < 0) return;
-    const int4 item = list[t];
+    const int4 entry = list[t];
+    const WorkTile item{entry.x, entry.y, entry.z};
     const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
-    const int d0 = item.z * BigCfg::BN;
+    const int d0 = item.ct * BigCfg::BN;
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint16_t *rp[BigCfg::CPW];
@@ -393,16 +453,14 @@ __global__ __launch_bounds__(256) void gateup_int4_kernel(
     const uint8_t *__restrict__ up_q, const uint16_t *__restrict__ up_s, int group,
     const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
-    int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+    const int32_t *__restrict__ perm, int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
 {
     static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
     constexpr int FC = C::BN / 2;
-    const int t = xcd_tile(n_items[1]);
-    if (t < 0) return;
-    const int4 item = list[t];
-    const int nt = item.z;
+    const WorkTile item = find_tile(count, E, T, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
+    if (item.e < 0) return;
+    const int nt = item.ct;
     const int R = T * K;
     const ExpertTile et = decode_tile(item, count, offset, E, T, R);
     const int f0 = nt * FC;
@@ -453,15 +511,14 @@ template <class C>
 __global__ __launch_bounds__(256) void down_int4_kernel(
     const uint16_t *__restrict__ h, const uint8_t *__restrict__ down_q, const uint16_t *__restrict__ down_s,
     int group, const uint16_t *__restrict__ s_down, const int32_t *__restrict__ count,
-    const int32_t *__restrict__ offset, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
-    int T, int D, int E, int K, int F, uint16_t *__restrict__ o, float *__restrict__ sx)
+    const int32_t *__restrict__ offset, int T, int D, int E, int K, int F, uint16_t *__restrict__ o,
+    float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const int t = xcd_tile(n_items[0]);
-    if (t < 0) return;
-    const int4 item = list[t];
+    const WorkTile item = find_tile(count, E, T, C::BM, (D + TILE_N - 1) / TILE_N);
+    if (item.e < 0) return;
     const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
-    const int d0 = item.z * C::BN;
+    const int d0 = item.ct * C::BN;
     const int ch0 = threadIdx.x & 7;
 
     const uint16_t *ap[C::A_PER_T];
@@ -664,12 +721,12 @@ static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     mk.mark(st);
     gateup_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
-        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.list_gu,
-        a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm,
+        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
         (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count, a.offset,
-        a.list_dn, a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
+        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 
@@ -679,6 +736,8 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
     const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     mk.mark(st);
+    ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, a.T, BigCfg::BM, ffn_col_tiles_gu(a.F),
+                                         ffn_col_tiles_dn(a.D), a.list_gu, a.list_dn, a.n_items);
     gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
         (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.list_gu,
@@ -699,12 +758,12 @@ static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t s
     mk.mark(st);
     gateup_int4_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         (const uint16_t *)a.x, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
-        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.list_gu,
-        a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm,
+        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_int4_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
         (const uint16_t *)a.h, a.down_q, a.down_s, a.group, (const uint16_t *)a.s_down, a.count, a.offset,
-        a.list_dn, a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
+        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 
@@ -714,10 +773,7 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
     const int R = T * K;
     StageMarks none;
     StageMarks &mk = a.marks ? *a.marks : none;
-    mk.mark(st);
     if (a.bf16) {
-        ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, T, a.bm, ffn_col_tiles_gu(F),
-                                             ffn_col_tiles_dn(D), a.list_gu, a.list_dn, a.n_items);
         if (a.use_int4) {
             if (a.bm == SmallCfg::BM)
                 launch_staged_int4<SmallCfg>(a, mk, st);

@@ -25,7 +25,7 @@ struct RouteLaunch {
     const void *x;
     const void *wr;
     const float *bias;
-    float *z;              // workspace [T][E]
+    float *z;              // workspace [router_splits][T][E]: partial logits
     int32_t *tile_count;   // workspace [perm_tiles(T)][E]
     int32_t *tile_base;    // workspace [perm_tiles(T)][E]
     int32_t *ids;
@@ -53,8 +53,8 @@ struct FfnLaunch {
     void *h;               // workspace [T*K + T][F]
     void *o;               // workspace [T*K][D]
     float *sx;             // workspace [T][D] (bf16 path): the shared expert's output
-    int4 *list_gu;         // workspace [ffn_max_tiles * ffn_col_tiles_gu]
-    int4 *list_dn;         // workspace [ffn_max_tiles * ffn_col_tiles_dn]
+    int4 *list_gu;         // workspace [ffn_max_tiles * ffn_col_tiles_gu] (256-row tiles)
+    int4 *list_dn;         // workspace [ffn_max_tiles * ffn_col_tiles_dn] (256-row tiles)
     int32_t *n_items;      // workspace [2]
     StageMarks *marks;     // nullable
 };
@@ -63,6 +63,7 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st);
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st);
 
 int perm_tiles(int T);
+int router_splits(int T, int D);
 int ffn_tile_rows(int T, int E, int K, int int4);
 long ffn_max_tiles(int T, int E, int K, int bm);
 int ffn_col_tiles_gu(int F);

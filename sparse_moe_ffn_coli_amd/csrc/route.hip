@@ -20,27 +20,33 @@ namespace coli {
 
 // ---------------------------------------------------------------------------
 // router logits, bf16 inputs, MFMA.  One workgroup per (32-token block,
-// 32*NF-expert block); the four waves split the reduction dimension into
-// quarters and stream their operands straight from global memory into MFMA
-// registers (each wave's data is its own, so no LDS staging).  The four
-// partial 32x64 blocks are added in LDS in wave order -- a fixed order, so
-// the logits are bitwise reproducible -- and the bias is added last.  Rows
-// past T and experts past E reread a valid row; their results are dropped.
+// 32*NF-expert block, reduction split); the four waves split the
+// workgroup's part of the reduction dimension into quarters and stream their
+// operands straight from global memory into MFMA registers (each wave's data
+// is its own, so no LDS staging).  The four partial blocks are added in LDS in
+// wave order and stored as split s's partial sums zp[s][t][e]; top-K adds
+// the splits in order s = 0, 1, ... and then the bias -- fixed orders, so the
+// logits are bitwise reproducible.  Small batches split the reduction over
+// several workgroups to occupy the GPU.  Rows past T and experts past E
+// reread a valid row; their results are dropped.
 // ---------------------------------------------------------------------------
 constexpr int RT_M = 32;
 constexpr int RT_BATCH = 8;         // reduction steps whose operands are loaded ahead
+constexpr int RT_MAX_SPLITS = 8;
 
 template <int NF>                    // 32-expert fragments per workgroup
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, const float *__restrict__ bias,
-    int T, int D, int E, float *__restrict__ z)
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int D, int E, int splits,
+    float *__restrict__ zp)
 {
     __shared__ float red[4 * NF * 16 * 64];         // [wave][frag][i][lane]
     const int n_nt = (E + 32 * NF - 1) / (32 * NF);
-    const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
+    const int n_mt = (T + RT_M - 1) / RT_M;
+    const int sp = blockIdx.x / (n_mt * n_nt), rem = blockIdx.x % (n_mt * n_nt);
+    const int mt = rem / n_nt, nt = rem % n_nt;
     const int t0 = mt * RT_M, e0 = nt * 32 * NF;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kq = D / 4, kbeg = wave * kq + 8 * (lane >> 5);
+    const int kq = D / (4 * splits), kbeg = (sp * 4 + wave) * kq + 8 * (lane >> 5);
     const uint16_t *pa = x + (size_t)min(t0 + (lane & 31), T - 1) * D + kbeg;
     const uint16_t *pb[NF];
 #pragma unroll
@@ -79,6 +85,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) red[((wave * NF + f) * 16 + i) * 64 + lane] = acc[f][i];
     __syncthreads();
+    float *z = zp + (size_t)sp * T * E;
     for (int q = threadIdx.x; q < NF * 16 * 64; q += 256) {
         const int f = q >> 10, i = (q >> 6) & 15, ln = q & 63;
         float v = red[((0 * NF + f) * 16 + i) * 64 + ln];
@@ -87,14 +94,23 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
         v += red[((3 * NF + f) * 16 + i) * 64 + ln];
         const int t = t0 + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
         const int e = e0 + f * 32 + (ln & 31);
-        if (t < T && e < E) z[(size_t)t * E + e] = v + bias[e];
+        if (t < T && e < E) z[(size_t)t * E + e] = v;
     }
 }
 
-// fp32 router: one thread per (token, expert), plain dot product.
-__global__ void router_logits_f32_kernel(const float *__restrict__ x, const float *__restrict__ wr,
-                                         const float *__restrict__ bias, int T, int D, int E,
-                                         float *__restrict__ z)
+// Reduction splits of the bf16 router: enough workgroups for small batches;
+// a split must cover whole 64-element quarters-of-16 (D / (64 splits) integral).
+int router_splits(int T, int D)
+{
+    const int want = (T <= 128) ? RT_MAX_SPLITS : (T <= 512) ? 4 : 1;
+    int s = want;
+    while (s > 1 && (D / 64) % s != 0) --s;
+    return s;
+}
+
+// fp32 router: one thread per (token, expert), plain dot product (one split).
+__global__ void router_logits_f32_kernel(const float *__restrict__ x, const float *__restrict__ wr, int T,
+                                         int D, int E, float *__restrict__ z)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)T * E) return;
@@ -102,7 +118,7 @@ __global__ void router_logits_f32_kernel(const float *__restrict__ x, const floa
     const float *xr = x + (size_t)t * D, *wrow = wr + (size_t)e * D;
     float acc = 0.f;
     for (int d = 0; d < D; ++d) acc = fmaf(xr[d], wrow[d], acc);
-    z[i] = acc + bias[e];
+    z[i] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -127,20 +143,34 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o)
 constexpr int TOPK_MAX_E = 1024;
 
 template <int SLOTS>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ z, int T, int E, int K,
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp, int splits,
+                                                   const float *__restrict__ bias, int T, int E, int K,
                                                    int32_t *__restrict__ ids, float *__restrict__ w)
 {
     const int lane = threadIdx.x & 63;
     const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
     if (t >= T) return;
-    const float *zt = z + (size_t)t * E;
 
-    // 0 marks an empty slot; every real logit maps above 0 (NaN aside)
+    // logit = (split 0 + split 1 + ...) + bias; 0 marks an empty slot, every
+    // real logit maps above 0 (NaN aside)
     uint32_t key[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
         const int e = lane + 64 * s;
-        key[s] = (e < E) ? ordered_bits(zt[e]) : 0u;
+        if (e < E) {
+            // all partials are loaded before the ordered sum
+            float part[RT_MAX_SPLITS];
+#pragma unroll
+            for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
+                part[sp] = (sp < splits) ? zp[((size_t)sp * T + t) * E + e] : 0.f;
+            float v = part[0];
+#pragma unroll
+            for (int sp = 1; sp < RT_MAX_SPLITS; ++sp)
+                if (sp < splits) v += part[sp];
+            key[s] = ordered_bits(v + bias[e]);
+        } else {
+            key[s] = 0u;
+        }
     }
     int sel_e[8];
     float sel_z[8];
@@ -289,6 +319,59 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
 }
 
 // ---------------------------------------------------------------------------
+// permutation of a small batch (T <= PERM_SMALL_T) in one workgroup of 1024
+// threads: the same bitmask construction over 16 waves of 64 tokens, the
+// counts, the exclusive scan over experts and the scatter, with no global
+// round trips between them.  The result is the same stable counting sort.
+// ---------------------------------------------------------------------------
+constexpr int PERM_SMALL_T = 1024;
+constexpr int PERM_SMALL_MAX_E = 512;         // 16 waves x E masks of 8 bytes in LDS
+
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int E, int K,
+                                                          int32_t *__restrict__ count,
+                                                          int32_t *__restrict__ offset,
+                                                          int32_t *__restrict__ perm,
+                                                          int32_t *__restrict__ inv)
+{
+    __shared__ uint64_t masks[16 * PERM_SMALL_MAX_E];
+    __shared__ int32_t sc[1024];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
+    __syncthreads();
+    if (tid < T)
+        for (int j = 0; j < K; ++j)
+            atomicOr((unsigned long long *)&masks[wave * E + ids[(size_t)tid * K + j]], 1ull << lane);
+    __syncthreads();
+    int c = 0;
+    if (tid < E)
+        for (int w2 = 0; w2 < 16; ++w2) c += __popcll(masks[w2 * E + tid]);
+    sc[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int v = (tid >= off) ? sc[tid - off] : 0;
+        __syncthreads();
+        sc[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) {
+        count[tid] = c;
+        offset[tid] = sc[tid] - c;
+        if (tid == E - 1) offset[E] = sc[tid];
+    }
+    if (tid < T) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        for (int j = 0; j < K; ++j) {
+            const int e = ids[(size_t)tid * K + j];
+            int rank = __popcll(masks[wave * E + e] & below);
+            for (int w2 = 0; w2 < wave; ++w2) rank += __popcll(masks[w2 * E + e]);
+            const int row = (e > 0 ? sc[e - 1] : 0) + rank;   // exclusive prefix + rank
+            perm[row] = tid * K + j;
+            inv[(size_t)tid * K + j] = row;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 int perm_tiles(int T) { return (T + PERM_TILE - 1) / PERM_TILE; }
@@ -312,35 +395,41 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
     StageMarks none;
     StageMarks &mk = a.marks ? *a.marks : none;
     mk.mark(st);
+    int splits = 1;
     if (a.bf16) {
-        // small batches: 32-expert blocks for more workgroups; large: 64
+        // small batches: 32-expert blocks and a split reduction for more
+        // workgroups; large: 64-expert blocks
+        splits = router_splits(T, D);
         const int n_mt = (T + RT_M - 1) / RT_M;
         if (T <= 512)
-            router_logits_bf16_kernel<1><<<n_mt * ((E + 31) / 32), 256, 0, st>>>(
-                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.bias, T, D, E, a.z);
+            router_logits_bf16_kernel<1><<<splits * n_mt * ((E + 31) / 32), 256, 0, st>>>(
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z);
         else
-            router_logits_bf16_kernel<2><<<n_mt * ((E + 63) / 64), 256, 0, st>>>(
-                (const uint16_t *)a.x, (const uint16_t *)a.wr, a.bias, T, D, E, a.z);
+            router_logits_bf16_kernel<2><<<splits * n_mt * ((E + 63) / 64), 256, 0, st>>>(
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z);
     } else {
         int64_t n = (int64_t)T * E;
         router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-            (const float *)a.x, (const float *)a.wr, a.bias, T, D, E, a.z);
+            (const float *)a.x, (const float *)a.wr, T, D, E, a.z);
     }
     mk.mark(st);
     {
         const int g = (T + 3) / 4, slots = (E + 63) / 64;
-        if (slots <= 1) topk_kernel<1><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
-        else if (slots <= 2) topk_kernel<2><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
-        else if (slots <= 4) topk_kernel<4><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
-        else if (slots <= 8) topk_kernel<8><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
-        else topk_kernel<16><<<g, 256, 0, st>>>(a.z, T, E, K, a.ids, a.w);
+        if (slots <= 1) topk_kernel<1><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 2) topk_kernel<2><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 4) topk_kernel<4><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 8) topk_kernel<8><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else topk_kernel<16><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+    }
+    mk.mark(st);
+    if (T <= PERM_SMALL_T && E <= PERM_SMALL_MAX_E) {
+        perm_small_kernel<<<1, 1024, 0, st>>>(a.ids, T, E, K, a.count, a.offset, a.perm, a.inv);
+        mk.mark(st);
+        return hipGetLastError();
     }
     const int ntiles = perm_tiles(T);
-    mk.mark(st);
     perm_hist_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_count);
-    mk.mark(st);
     perm_scan_kernel<<<1, 1024, 0, st>>>(a.tile_count, ntiles, E, a.tile_base, a.count, a.offset);
-    mk.mark(st);
     perm_scatter_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_base, a.perm, a.inv);
     mk.mark(st);
     return hipGetLastError();
