@@ -124,7 +124,7 @@ def recorded_traffic(workload, kernel_prefix):
     if summ.get("sources_sha256_16") != sources_hash():
         return None
     for name, v in summ["kernels"].items():
-        if name.split("::")[-1].startswith(kernel_prefix):
+        if name.split("<")[0].split("::")[-1].startswith(kernel_prefix):
             return v["hbm_bytes"]
     return None
 
