@@ -67,7 +67,7 @@ FfnWs ffn_ws(const coli_moe_shape *s, int quant)
     w.list_gu = align_up(w.sx + T * D * 4);
     w.list_dn = align_up(w.list_gu + max_tiles * (size_t)coli::ffn_col_tiles_gu(s->F) * 16);
     w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * 16);
-    w.total = align_up(w.n_items + 16);
+    w.total = align_up(w.n_items + 20 * 4);
     return w;
 }
 

@@ -125,8 +125,59 @@ __device__ __forceinline__ WorkTile find_tile(const int32_t *__restrict__ count,
 
 // The 256 x 256 kernels run one workgroup per CU, so nothing hides a
 // per-tile search there: their tiles come from a list built beforehand by
-// one small kernel in the same order (n_items[0] = entries of the down list,
-// n_items[1] = entries of the gate+up list).
+// one small kernel in the same order.  Each list is cut into 8 contiguous
+// per-XCD ranges of equal estimated cost -- a tile costs TILE_COST0 + its
+// real rows (the fixed part is the weight stream every tile pays; a 32-row
+// tile takes about half as long as a 256-row one) -- and the workgroups of
+// XCD x walk range x.  n_items: [0] entries of the down list, [1] of the
+// gate+up list, [2..10] gate+up range starts (x = 0..8), [11..19] down.
+constexpr int TILE_COST0 = 208;
+
+// Sets starts[0..8]: entry q goes to XCD floor(8 * (cost of entries before q) / total).
+__device__ __forceinline__ void xcd_split(const int4 *list, int n, const int32_t *__restrict__ count, int E,
+                                          int T, int BM, int32_t *__restrict__ starts)
+{
+    __shared__ int32_t csum[1024];
+    const int tid = threadIdx.x;
+    const int per = (n + 1023) / 1024;
+    const int q0 = min(tid * per, n), q1 = min(q0 + per, n);
+    auto cost = [&](int q) {
+        const int4 en = list[q];
+        const int cnt = (en.x == E) ? T : count[en.x];
+        return TILE_COST0 + min(BM, cnt - en.y);
+    };
+    int c = 0;
+    for (int q = q0; q < q1; ++q) c += cost(q);
+    csum[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int v = (tid >= off) ? csum[tid - off] : 0;
+        __syncthreads();
+        csum[tid] += v;
+        __syncthreads();
+    }
+    const long total = csum[1023];
+    const long tot = max(total, 1L);
+    long before = csum[tid] - c;                  // cost of entries before q0
+    // XCD of entry q0 - 1 (-1 for the first entry), so that a boundary on
+    // this chunk's first entry is written by this thread
+    int prev = -1;
+    if (q0 > 0 && q0 < n) prev = (int)min(7L, (before - cost(q0 - 1)) * 8 / tot);
+    for (int q = q0; q < q1; ++q) {
+        const int xq = (int)min(7L, before * 8 / tot);
+        for (int xx = prev + 1; xx <= xq; ++xx) starts[xx] = q;    // first entry of XCD xx
+        prev = xq;
+        before += cost(q);
+    }
+    // the thread holding the last entry closes the ranges: XCDs after its
+    // XCD are empty and every range ends at n
+    if (q0 < q1 && q1 == n)
+        for (int xx = prev + 1; xx <= 8; ++xx) starts[xx] = n;
+    if (n == 0 && tid == 0)
+        for (int xx = 0; xx <= 8; ++xx) starts[xx] = 0;
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
                                                          int BM, int nnt_gu, int nnt_dn,
                                                          int4 *__restrict__ list_gu,
@@ -177,6 +228,9 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
         n_items[0] = n_dn;
         n_items[1] = n_gu;
     }
+    __syncthreads();
+    xcd_split(list_gu, n_gu, count, E, T, BM, n_items + 2);
+    xcd_split(list_dn, n_dn, count, E, T, BM, n_items + 2 + 9);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,8 +379,11 @@ __global__ __launch_bounds__(256) void down_kernel(
 
 // ---------------------------------------------------------------------------
 // 1/2 on the large-tile engine (row-heavy batches): 256 x 256 tiles, eight
-// waves.  Each wave runs the variant for its number of real 32-row fragments.
+// waves.  A tile with at most 32 real rows runs the engine's streaming mode;
+// otherwise each wave runs the variant for its number of real 32-row
+// fragments.
 // ---------------------------------------------------------------------------
+constexpr int BIG_LDS_BYTES = (BigCfg::LDS_BYTES > StreamCfg::LDS_BYTES) ? BigCfg::LDS_BYTES : StreamCfg::LDS_BYTES;
 __device__ __forceinline__ int big_wave_fragments(int rows, int wm)
 {
     return min(max((rows - wm * 64 + 31) >> 5, 0), 2);
@@ -355,16 +412,13 @@ __device__ __forceinline__ void gateup_big_body(const uint16_t *const (&rp)[BigC
         }
 }
 
-__global__ __launch_bounds__(512) void gateup_big_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
+__device__ __forceinline__ void gateup_big_tile(
+    int t, const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
     const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
-    int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+    const int32_t *__restrict__ perm, const int4 *__restrict__ list, int T, int D, int E, int K, int F,
+    char *lds, uint16_t *__restrict__ h)
 {
-    __shared__ __attribute__((aligned(1024))) char lds[BigCfg::LDS_BYTES];
-    const int t = xcd_tile(n_items[1]);
-    if (t < 0) return;
     const int4 entry = list[t];
     const WorkTile item{entry.x, entry.y, entry.z};
     const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
@@ -382,6 +436,29 @@ __global__ __launch_bounds__(512) void gateup_big_kernel(
         const int tok = et.shared ? r : perm[et.base + r] / K;
         rp[j] = x + (size_t)tok * D + ch * 8;
         rp[BigCfg::CPO + j] = gateup_b_row(G, U, f0, row, D, F) + ch * 8;
+    }
+    if (et.cnt - et.m0 <= 32) {
+        const int row = stream_a_row(w);
+        const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
+        const int tok = et.shared ? r : perm[et.base + r] / K;
+        const uint16_t *ra = x + (size_t)tok * D + big_copy_chunk<BigCfg>(row) * 8;
+        const uint16_t *rb[4] = {rp[BigCfg::CPO], rp[BigCfg::CPO + 1], rp[BigCfg::CPO + 2], rp[BigCfg::CPO + 3]};
+        f32x16 acc[4];
+        stream_mainloop(ra, rb, D, w, lds, acc);
+        if ((w >> 1) != 0) return;
+        const int lane = threadIdx.x & 63, wn = w & 1;
+#pragma unroll
+        for (int n = 0; n < 4; n += 2) {
+            const int f = f0 + (wn * 2 + (n >> 1)) * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rr = et.m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (rr < et.cnt && f < F)
+                    h[(size_t)(et.base + rr) * F + f] =
+                        f32_to_bf16_bits(swiglu_clamped(acc[n][i], acc[n + 1][i]));
+            }
+        }
+        return;
     }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
     if (nfw == 2) gateup_big_body<2>(rp, et, f0, D, F, w, lds, h);
@@ -410,15 +487,11 @@ __device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg
         }
 }
 
-__global__ __launch_bounds__(512) void down_big_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int K, int F,
-    uint16_t *__restrict__ o, float *__restrict__ sx)
+__device__ __forceinline__ void down_big_tile(
+    int t, const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ offset, const int4 *__restrict__ list,
+    int T, int D, int E, int K, int F, char *lds, uint16_t *__restrict__ o, float *__restrict__ sx)
 {
-    __shared__ __attribute__((aligned(1024))) char lds[BigCfg::LDS_BYTES];
-    const int t = xcd_tile(n_items[0]);
-    if (t < 0) return;
     const int4 entry = list[t];
     const WorkTile item{entry.x, entry.y, entry.z};
     const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
@@ -436,10 +509,63 @@ __global__ __launch_bounds__(512) void down_big_kernel(
         const int d = min(d0 + row, D - 1);       // rows past D reread the last one
         rp[BigCfg::CPO + j] = W + (size_t)d * F + ch * 8;
     }
+    if (et.cnt - et.m0 <= 32) {
+        const int row = stream_a_row(w);
+        const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
+        const uint16_t *ra = h + (size_t)(et.base + r) * F + big_copy_chunk<BigCfg>(row) * 8;
+        const uint16_t *rb[4] = {rp[BigCfg::CPO], rp[BigCfg::CPO + 1], rp[BigCfg::CPO + 2], rp[BigCfg::CPO + 3]};
+        f32x16 acc[4];
+        stream_mainloop(ra, rb, F, w, lds, acc);
+        if ((w >> 1) != 0) return;
+        const int lane = threadIdx.x & 63, wn = w & 1;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int d = d0 + (wn * 4 + n) * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rr = et.m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (rr < et.cnt && d < D) store_down(et, rr, d, D, acc[n][i], o, sx);
+            }
+        }
+        return;
+    }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
     if (nfw == 2) down_big_body<2>(rp, et, d0, D, F, w, lds, o, sx);
     else if (nfw == 1) down_big_body<1>(rp, et, d0, D, F, w, lds, o, sx);
     else down_big_body<0>(rp, et, d0, D, F, w, lds, o, sx);
+}
+
+// Workgroup (x = blockIdx % 8, its XCD) walks range x of the list with a
+// stride of gridDim / 8 workgroups; the barrier ends each tile's use of LDS.
+__global__ __launch_bounds__(512) void gateup_big_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
+    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
+    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
+    int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[BIG_LDS_BYTES];
+    const int xc = blockIdx.x & 7;
+    const int beg = max(n_items[2 + xc], 0), end = min(n_items[2 + xc + 1], n_items[1]);
+    for (int t = beg + (blockIdx.x >> 3); t < end; t += gridDim.x >> 3) {
+        gateup_big_tile(t, x, gate, up, s_gate, s_up, count, offset, perm, list, T, D, E, K, F, lds, h);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(512) void down_big_kernel(
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int K, int F,
+    uint16_t *__restrict__ o, float *__restrict__ sx)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[BIG_LDS_BYTES];
+    const int xc = blockIdx.x & 7;
+    const int beg = max(n_items[11 + xc], 0), end = min(n_items[11 + xc + 1], n_items[0]);
+    for (int t = beg + (blockIdx.x >> 3); t < end; t += gridDim.x >> 3) {
+        down_big_tile(t, h, down, s_down, count, offset, list, T, D, E, K, F, lds, o, sx);
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -55,7 +55,7 @@ struct FfnLaunch {
     float *sx;             // workspace [T][D] (bf16 path): the shared expert's output
     int4 *list_gu;         // workspace [ffn_max_tiles * ffn_col_tiles_gu] (256-row tiles)
     int4 *list_dn;         // workspace [ffn_max_tiles * ffn_col_tiles_dn] (256-row tiles)
-    int32_t *n_items;      // workspace [2]
+    int32_t *n_items;      // workspace [20]: list lengths and per-XCD range starts
     StageMarks *marks;     // nullable
 };
 

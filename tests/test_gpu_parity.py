@@ -29,21 +29,23 @@ def _report(label, err):
 # small shapes: several tiles, ragged tails, full oracle
 # ---------------------------------------------------------------------------
 SMALL = [
-    # cid, T, D, E, K, F, dtype  -- rows per expert decide the tile height
-    (101, 200, 256, 40, 8, 192, "bf16"),     # 40 rows/expert: 128-row tiles, ragged
-    (102, 100, 128, 288, 8, 128, "bf16"),    # ~3 rows/expert: 16-row tiles
-    (103, 67, 192, 24, 8, 64, "f32"),
-    (104, 130, 64, 16, 8, 64, "bf16"),       # minimum widths, heavy load per expert
+    # cid, T, D, E, K, F, dtype, router bias -- rows per expert decide the tile engine
+    (101, 200, 256, 40, 8, 192, "bf16", "uniform"),   # 40 rows/expert: 256-row tiles, ragged
+    (102, 100, 128, 288, 8, 128, "bf16", "uniform"),  # ~3 rows/expert: 32-row tiles
+    (103, 67, 192, 24, 8, 64, "f32", "uniform"),
+    (104, 130, 64, 16, 8, 64, "bf16", "uniform"),     # minimum widths, heavy load per expert
+    (105, 600, 256, 48, 8, 192, "bf16", "zipf"),      # skewed: full, partial and <= 32-row tiles
 ]
 
 
-@pytest.mark.parametrize("cid,T,D,E,K,F,dt", SMALL)
-def test_small_shapes(cid, T, D, E, K, F, dt):
-    cfg = custom_cfg(cid, T, D, E, K, F, dt)
+@pytest.mark.parametrize("cid,T,D,E,K,F,dt,bias", SMALL)
+def test_small_shapes(cid, T, D, E, K, F, dt, bias):
+    cfg = custom_cfg(cid, T, D, E, K, F, dt, bias=bias)
     W = make_inputs(cfg)
     got = run_gpu(W, cfg)
     ref = run_oracle(W, cfg)
-    _report(f"small cid={cid}", compare(got, ref, cfg, label=f"cid={cid}"))
+    _report(f"small cid={cid} counts {sorted(ref['count'].tolist())[-3:]}..{sorted(ref['count'].tolist())[:3]}",
+            compare(got, ref, cfg, label=f"cid={cid}"))
 
 
 # ---------------------------------------------------------------------------
