@@ -138,6 +138,7 @@ __device__ __forceinline__ void xcd_split(const int4 *list, int n, const int32_t
                                           int T, int BM, int32_t *__restrict__ starts)
 {
     __shared__ int32_t csum[1024];
+    __shared__ int32_t ws[16];
     const int tid = threadIdx.x;
     const int per = (n + 1023) / 1024;
     const int q0 = min(tid * per, n), q1 = min(q0 + per, n);
@@ -148,14 +149,8 @@ __device__ __forceinline__ void xcd_split(const int4 *list, int n, const int32_t
     };
     int c = 0;
     for (int q = q0; q < q1; ++q) c += cost(q);
-    csum[tid] = c;
+    csum[tid] = block_scan_incl_1024(c, ws);
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = (tid >= off) ? csum[tid - off] : 0;
-        __syncthreads();
-        csum[tid] += v;
-        __syncthreads();
-    }
     const long total = csum[1023];
     const long tot = max(total, 1L);
     long before = csum[tid] - c;                  // cost of entries before q0
@@ -187,15 +182,10 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
     // sc[e] = row tiles of routed experts 0..e (inclusive scan); the shared
     // expert's ceil(T/BM) row tiles follow them
     __shared__ int32_t sc[1024];
+    __shared__ int32_t ws[16];
     const int tid = threadIdx.x;
-    sc[tid] = (tid < E) ? (count[tid] + BM - 1) / BM : 0;
+    sc[tid] = block_scan_incl_1024((tid < E) ? (count[tid] + BM - 1) / BM : 0, ws);
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = (tid >= off) ? sc[tid - off] : 0;
-        __syncthreads();
-        sc[tid] += v;
-        __syncthreads();
-    }
     const int routed = sc[1023];
     const int mt_sh = (T + BM - 1) / BM;
     // expert owning row tile index i < routed: the first e with sc[e] > i

@@ -152,25 +152,29 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
     if (t >= T) return;
 
     // logit = (split 0 + split 1 + ...) + bias; 0 marks an empty slot, every
-    // real logit maps above 0 (NaN aside)
+    // real logit maps above 0 (NaN aside).  Every partial and bias of the
+    // token is loaded before any sum, so the loads cost one memory latency.
+    const float *zs[RT_MAX_SPLITS];                 // this lane's logits in split sp
+#pragma unroll
+    for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
+        zs[sp] = zp + ((size_t)min(sp, splits - 1) * T + t) * E + lane;
+    float part[SLOTS][RT_MAX_SPLITS], bs[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+        const bool in = lane + 64 * s < E;
+        bs[s] = in ? bias[lane + 64 * s] : 0.f;
+#pragma unroll
+        for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
+            part[s][sp] = in ? zs[sp][64 * s] : 0.f;   // splits past the last reread it (unused)
+    }
     uint32_t key[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
-        const int e = lane + 64 * s;
-        if (e < E) {
-            // all partials are loaded before the ordered sum
-            float part[RT_MAX_SPLITS];
+        float v = part[s][0];
 #pragma unroll
-            for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
-                part[sp] = (sp < splits) ? zp[((size_t)sp * T + t) * E + e] : 0.f;
-            float v = part[0];
-#pragma unroll
-            for (int sp = 1; sp < RT_MAX_SPLITS; ++sp)
-                if (sp < splits) v += part[sp];
-            key[s] = ordered_bits(v + bias[e]);
-        } else {
-            key[s] = 0u;
-        }
+        for (int sp = 1; sp < RT_MAX_SPLITS; ++sp)
+            if (sp < splits) v += part[s][sp];
+        key[s] = (lane + 64 * s < E) ? ordered_bits(v + bs[s]) : 0u;
     }
     int sel_e[8];
     float sel_z[8];
@@ -271,28 +275,38 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t *__restri
                                                          int32_t *__restrict__ offset)
 {
     __shared__ int32_t sc[TOPK_MAX_E];
+    __shared__ int32_t ws[16];
     const int tid = threadIdx.x;
+    // the per-tile counts are read eight tiles at a time (independent loads)
     int c = 0;
     if (tid < E) {
-        for (int tl = 0; tl < ntiles; ++tl) c += tile_count[(size_t)tl * E + tid];
+        for (int tl0 = 0; tl0 < ntiles; tl0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = (tl0 + k < ntiles) ? tile_count[(size_t)(tl0 + k) * E + tid] : 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c += v[k];
+        }
         count[tid] = c;
     }
-    sc[tid] = (tid < E) ? c : 0;
+    sc[tid] = block_scan_incl_1024((tid < E) ? c : 0, ws);
     __syncthreads();
-    // inclusive Hillis-Steele scan over 1024 entries
-    for (int off = 1; off < TOPK_MAX_E; off <<= 1) {
-        int v = (tid >= off) ? sc[tid - off] : 0;
-        __syncthreads();
-        sc[tid] += v;
-        __syncthreads();
-    }
     if (tid < E) {
         int base = sc[tid] - c;           // exclusive prefix
         offset[tid] = base;
         if (tid == E - 1) offset[E] = sc[tid];
-        for (int tl = 0; tl < ntiles; ++tl) {
-            tile_base[(size_t)tl * E + tid] = base;
-            base += tile_count[(size_t)tl * E + tid];
+        for (int tl0 = 0; tl0 < ntiles; tl0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = (tl0 + k < ntiles) ? tile_count[(size_t)(tl0 + k) * E + tid] : 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (tl0 + k < ntiles) {
+                    tile_base[(size_t)(tl0 + k) * E + tid] = base;
+                    base += v[k];
+                }
         }
     }
 }
@@ -335,6 +349,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
 {
     __shared__ uint64_t masks[16 * PERM_SMALL_MAX_E];
     __shared__ int32_t sc[1024];
+    __shared__ int32_t ws[16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
     __syncthreads();
@@ -345,14 +360,8 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
     int c = 0;
     if (tid < E)
         for (int w2 = 0; w2 < 16; ++w2) c += __popcll(masks[w2 * E + tid]);
-    sc[tid] = c;
+    sc[tid] = block_scan_incl_1024(c, ws);
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = (tid >= off) ? sc[tid - off] : 0;
-        __syncthreads();
-        sc[tid] += v;
-        __syncthreads();
-    }
     if (tid < E) {
         count[tid] = c;
         offset[tid] = sc[tid] - c;
