@@ -134,19 +134,14 @@ __device__ __forceinline__ WorkTile find_tile(const int32_t *__restrict__ count,
 constexpr int TILE_COST0 = 208;
 
 // Sets starts[0..8]: entry q goes to XCD floor(8 * (cost of entries before q) / total).
-__device__ __forceinline__ void xcd_split(const int4 *list, int n, const int32_t *__restrict__ count, int E,
-                                          int T, int BM, int32_t *__restrict__ starts)
+template <class Cost>
+__device__ __forceinline__ void xcd_split(int n, Cost &&cost, int32_t *__restrict__ starts)
 {
     __shared__ int32_t csum[1024];
     __shared__ int32_t ws[16];
     const int tid = threadIdx.x;
     const int per = (n + 1023) / 1024;
     const int q0 = min(tid * per, n), q1 = min(q0 + per, n);
-    auto cost = [&](int q) {
-        const int4 en = list[q];
-        const int cnt = (en.x == E) ? T : count[en.x];
-        return TILE_COST0 + min(BM, cnt - en.y);
-    };
     int c = 0;
     for (int q = q0; q < q1; ++q) c += cost(q);
     csum[tid] = block_scan_incl_1024(c, ws);
@@ -173,54 +168,83 @@ __device__ __forceinline__ void xcd_split(const int4 *list, int n, const int32_t
     __syncthreads();
 }
 
+// One workgroup.  The counts are read from global memory once; the owner of
+// every row tile goes into an LDS table, so each list entry is computed once,
+// from LDS alone, together with its cost, which stays in LDS for the split.
+// Lists longer than the LDS tables recompute entries by binary search.
+constexpr int TILES_LDS_ROWS = 4096;     // row tiles with an owner entry in LDS
+constexpr int TILES_LDS_COST = 8192;     // entries per list with a cost in LDS
+
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
                                                          int BM, int nnt_gu, int nnt_dn,
                                                          int4 *__restrict__ list_gu,
                                                          int4 *__restrict__ list_dn,
                                                          int32_t *__restrict__ n_items)
 {
-    // sc[e] = row tiles of routed experts 0..e (inclusive scan); the shared
-    // expert's ceil(T/BM) row tiles follow them
+    // cnt[e]: rows of expert e; sc[e] = row tiles of routed experts 0..e
+    // (inclusive scan); the shared expert's ceil(T/BM) row tiles follow them
+    __shared__ int32_t cnt[1024];
     __shared__ int32_t sc[1024];
     __shared__ int32_t ws[16];
+    __shared__ int16_t owner_s[TILES_LDS_ROWS];
+    __shared__ int16_t cost_gu[TILES_LDS_COST], cost_dn[TILES_LDS_COST];
     const int tid = threadIdx.x;
-    sc[tid] = block_scan_incl_1024((tid < E) ? (count[tid] + BM - 1) / BM : 0, ws);
+    const int c = (tid < E) ? count[tid] : 0;
+    cnt[tid] = c;
+    const int mte_t = (c + BM - 1) / BM;
+    sc[tid] = block_scan_incl_1024(mte_t, ws);
     __syncthreads();
     const int routed = sc[1023];
     const int mt_sh = (T + BM - 1) / BM;
-    // expert owning row tile index i < routed: the first e with sc[e] > i
-    auto owner = [&](int i) {
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (sc[mid] > i) hi = mid; else lo = mid + 1;
+    const bool table = routed <= TILES_LDS_ROWS;
+    if (table && tid < E)
+        for (int i = sc[tid] - mte_t; i < sc[tid]; ++i) owner_s[i] = (int16_t)tid;
+    __syncthreads();
+    // entry q of a list with nnt column tiles -> (expert, first row, column tile)
+    auto entry = [&](int q, int nnt) {
+        const int i = q / nnt;
+        int e = E;
+        if (i < routed) {
+            if (table) {
+                e = owner_s[i];
+            } else {                              // the first e with sc[e] > i
+                int lo = 0, hi = E - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (sc[mid] > i) hi = mid; else lo = mid + 1;
+                }
+                e = lo;
+            }
         }
-        return lo;
+        const int mte = (e == E) ? mt_sh : (cnt[e] + BM - 1) / BM;
+        const int first = (e == E) ? routed : sc[e] - mte;
+        const int2 mn = block_order(q - first * nnt, mte, nnt);
+        return make_int4(e, mn.x * BM, mn.y, 0);
+    };
+    auto cost_of = [&](const int4 &en) {
+        const int rows = (en.x == E) ? T : cnt[en.x];
+        return TILE_COST0 + min(BM, rows - en.y);
     };
     const int n_gu = (routed + mt_sh) * nnt_gu, n_dn = (routed + mt_sh) * nnt_dn;
     for (int q = tid; q < n_gu; q += 1024) {
-        const int i = q / nnt_gu;
-        const int e = (i < routed) ? owner(i) : E;
-        const int mte = (e == E) ? mt_sh : (count[e] + BM - 1) / BM;
-        const int first = (e == E) ? routed : sc[e] - mte;
-        const int2 mn = block_order(q - first * nnt_gu, mte, nnt_gu);
-        list_gu[q] = make_int4(e, mn.x * BM, mn.y, 0);
+        const int4 en = entry(q, nnt_gu);
+        list_gu[q] = en;
+        if (q < TILES_LDS_COST) cost_gu[q] = (int16_t)cost_of(en);
     }
     for (int q = tid; q < n_dn; q += 1024) {
-        const int i = q / nnt_dn;
-        const int e = (i < routed) ? owner(i) : E;
-        const int mte = (e == E) ? mt_sh : (count[e] + BM - 1) / BM;
-        const int first = (e == E) ? routed : sc[e] - mte;
-        const int2 mn = block_order(q - first * nnt_dn, mte, nnt_dn);
-        list_dn[q] = make_int4(e, mn.x * BM, mn.y, 0);
+        const int4 en = entry(q, nnt_dn);
+        list_dn[q] = en;
+        if (q < TILES_LDS_COST) cost_dn[q] = (int16_t)cost_of(en);
     }
     if (tid == 0) {
         n_items[0] = n_dn;
         n_items[1] = n_gu;
     }
     __syncthreads();
-    xcd_split(list_gu, n_gu, count, E, T, BM, n_items + 2);
-    xcd_split(list_dn, n_dn, count, E, T, BM, n_items + 2 + 9);
+    xcd_split(n_gu, [&](int q) { return q < TILES_LDS_COST ? (int)cost_gu[q] : cost_of(entry(q, nnt_gu)); },
+              n_items + 2);
+    xcd_split(n_dn, [&](int q) { return q < TILES_LDS_COST ? (int)cost_dn[q] : cost_of(entry(q, nnt_dn)); },
+              n_items + 2 + 9);
 }
 
 // ---------------------------------------------------------------------------

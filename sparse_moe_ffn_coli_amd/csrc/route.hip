@@ -16,6 +16,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace coli {
 
 // ---------------------------------------------------------------------------
@@ -98,11 +100,141 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// router logits, bf16 inputs, large batches.  One workgroup per (32-token
+// block, reduction split) covers every expert, so each token row is fetched
+// once per split and the router matrix is shared by all token blocks from
+// L2.  Each 64-wide reduction step copies the block's 32 token rows and the
+// E router rows (padded to 32) global -> LDS, eight 128-byte rows per copy
+// instruction, through a ring of up to RL_MAX_STAGES stages (as many as fit
+// in LDS).  Rows are XOR-swizzled in 16-byte chunks so the fragment reads
+// are free of bank conflicts.  Wave w computes expert fragments w, w+4, ...
+// over the whole split; split s's partial sums go to zp[s][t][e] (top-K adds
+// the splits in order and then the bias).
+// ---------------------------------------------------------------------------
+constexpr int RL_BK = 64;
+constexpr int RL_MAX_E = 512;
+constexpr int RL_MAX_STAGES = 4;
+constexpr int RL_LDS_BYTES = 160 * 1024;
+constexpr int RL_MIN_T = 513;       // smaller batches use the register-streamed kernel above
+
+// Stages of the ring for E experts (the stage holds 32 + E rounded up to 32 rows).
+static int router_lds_stages(int E)
+{
+    const int stage = (32 + (E + 31) / 32 * 32) * 128;
+    return std::min(RL_MAX_STAGES, RL_LDS_BYTES / stage);
+}
+
+// s_waitcnt needs an immediate: wave-uniform n in [0, 63] via a jump table.
+__device__ __forceinline__ void wait_vmcnt_rt(int n)
+{
+    switch (n) {
+#define COLI_VM(i) case i: wait_vmcnt_c<i>(); break;
+        COLI_VM(0) COLI_VM(1) COLI_VM(2) COLI_VM(3) COLI_VM(4) COLI_VM(5) COLI_VM(6) COLI_VM(7)
+        COLI_VM(8) COLI_VM(9) COLI_VM(10) COLI_VM(11) COLI_VM(12) COLI_VM(13) COLI_VM(14) COLI_VM(15)
+        COLI_VM(16) COLI_VM(17) COLI_VM(18) COLI_VM(19) COLI_VM(20) COLI_VM(21) COLI_VM(22) COLI_VM(23)
+        COLI_VM(24) COLI_VM(25) COLI_VM(26) COLI_VM(27) COLI_VM(28) COLI_VM(29) COLI_VM(30) COLI_VM(31)
+        COLI_VM(32) COLI_VM(33) COLI_VM(34) COLI_VM(35)
+#undef COLI_VM
+        default: wait_vmcnt_c<0>(); break;
+    }
+}
+
+template <int NFW>                    // expert fragments per wave: nfrag <= 4 * NFW
+__global__ __launch_bounds__(256) void router_logits_lds_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int D, int E, int splits,
+    int ns, float *__restrict__ zp)
+{
+    constexpr int CPW_MAX = 1 + 4 * NFW;
+    __shared__ __attribute__((aligned(1024))) char lds[RL_LDS_BYTES];
+    const int nfrag = (E + 31) / 32;
+    const int rows = 32 + nfrag * 32;             // LDS rows per stage: tokens, then experts
+    const int stage_bytes = rows * 128;
+    const int cpw = rows / 32;                    // copy instructions per wave per stage (same for all waves)
+    const int n_mt = (T + 31) / 32;
+    const int sp = blockIdx.x / n_mt, mt = blockIdx.x % n_mt;
+    const int t0 = mt * 32;
+    const int kq = D / splits, nk = kq / RL_BK;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // copy j of wave w fills LDS rows (w + 4j) * 8 .. +7; lane l takes row
+    // (w + 4j) * 8 + l / 8, whose chunk position l % 8 holds the row's global
+    // chunk (l % 8) ^ ((row / 2) % 8).  Rows past T or E reread a valid row.
+    const uint16_t *src[CPW_MAX];
+#pragma unroll
+    for (int j = 0; j < CPW_MAX; ++j) {
+        const int r = min((w + 4 * j) * 8, rows - 8) + (lane >> 3);
+        src[j] = ((r < 32) ? x + (size_t)min(t0 + r, T - 1) * D : wr + (size_t)min(r - 32, E - 1) * D)
+                 + (size_t)sp * kq + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+    }
+    // the workgroups start their reduction at different steps (rot), so the
+    // ones running together read different columns of the shared router rows
+    const int rot = mt % nk;
+    auto issue = [&](int s) {
+        char *st = lds + (s % ns) * stage_bytes;
+        const int kb = (s + rot < nk) ? s + rot : s + rot - nk;
+#pragma unroll
+        for (int j = 0; j < CPW_MAX; ++j)
+            if (j < cpw)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(src[j] + kb * RL_BK),
+                    (__attribute__((address_space(3))) void *)(st + (w + 4 * j) * 1024), 16, 0, 0);
+    };
+
+    // fragment i of wave w: experts (w + 4i) * 32 ..; past the last fragment
+    // the wave recomputes the last one and drops the result
+    int brow[NFW];
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) brow[i] = 32 + min(w + 4 * i, nfrag - 1) * 32 + (lane & 31);
+    f32x16 acc[NFW];
+#pragma unroll
+    for (int i = 0; i < NFW; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+
+    for (int s = 0; s < min(ns - 1, nk); ++s) issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt_rt(min(ns - 2, nk - 1 - kt) * cpw);      // this wave's copies of stage kt landed
+        asm volatile("s_barrier" ::: "memory");             // everyone's; stage kt-1 fully read
+        if (kt + ns - 1 < nk) issue(kt + ns - 1);
+        const char *st = lds + (kt % ns) * stage_bytes;
+        bf16x8 a[RL_BK / 16], b[RL_BK / 16][NFW];
+#pragma unroll
+        for (int kk = 0; kk < RL_BK / 16; ++kk) {
+            const int c = kk * 2 + (lane >> 5);
+            a[kk] = *reinterpret_cast<const bf16x8 *>(st + swz(lane & 31, c) * 2);
+#pragma unroll
+            for (int i = 0; i < NFW; ++i) b[kk][i] = *reinterpret_cast<const bf16x8 *>(st + swz(brow[i], c) * 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // all of the stage's fragment reads in flight before its MFMAs
+#pragma unroll
+        for (int kk = 0; kk < RL_BK / 16; ++kk)
+#pragma unroll
+            for (int i = 0; i < NFW; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b[kk][i], acc[i], 0, 0, 0);
+    }
+    float *z = zp + (size_t)sp * T * E;
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) {
+        const int f = w + 4 * i;
+        if (f >= nfrag) continue;
+        const int e = f * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int t = t0 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            if (t < T && e < E) z[(size_t)t * E + e] = acc[i][j];
+        }
+    }
+}
+
 // Reduction splits of the bf16 router: enough workgroups for small batches;
 // a split must cover whole 64-element quarters-of-16 (D / (64 splits) integral).
 int router_splits(int T, int D)
 {
-    const int want = (T <= 128) ? RT_MAX_SPLITS : (T <= 512) ? 4 : 1;
+    int want = (T <= 128) ? RT_MAX_SPLITS : (T <= 512) ? 4 : 1;
+    if (T >= RL_MIN_T)                          // one 32-token block per workgroup: aim for 256
+        while (want < 4 && (T + 31) / 32 * want < 256) want *= 2;
     int s = want;
     while (s > 1 && (D / 64) % s != 0) --s;
     return s;
@@ -123,10 +255,15 @@ __global__ void router_logits_f32_kernel(const float *__restrict__ x, const floa
 
 // ---------------------------------------------------------------------------
 // top-K: one wave per token.  Lane l holds the logits of experts l, l+64, ...
-// as order-preserving unsigned images of the fp32 values.  Each of the K
-// rounds takes the wave-wide maximum value, then, among the lanes holding
-// it, the lowest expert index (ties go to the lower index), and removes that
-// expert.  Both reductions run on DPP lane permutations.
+// (slot s: expert 64 s + l) as order-preserving unsigned images of the fp32
+// values.  The K-th largest image tau is found bit by bit, most significant
+// first: a candidate bit stays set when at least K images are >= the
+// candidate (counted with one ballot per slot), so after 32 steps tau is
+// the K-th largest value.  The chosen experts are every image above tau and,
+// of those equal to tau, the lowest expert indices until K are taken (ties go
+// to the lower index).  Since the index is 64 s + l, slot-major lane order is
+// ascending index order, so each chosen expert's output position is a
+// prefix popcount of the chosen masks: the ids come out ascending.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ordered_bits(float f)
 {
@@ -147,17 +284,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
                                                    const float *__restrict__ bias, int T, int E, int K,
                                                    int32_t *__restrict__ ids, float *__restrict__ w)
 {
-    const int lane = threadIdx.x & 63;
+    __shared__ int32_t sel_e_s[4][8];
+    __shared__ float sel_z_s[4][8];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
-    if (t >= T) return;
+    if (t >= T) return;                           // whole waves: t is uniform in a wave
 
     // logit = (split 0 + split 1 + ...) + bias; 0 marks an empty slot, every
     // real logit maps above 0 (NaN aside).  Every partial and bias of the
     // token is loaded before any sum, so the loads cost one memory latency.
-    const float *zs[RT_MAX_SPLITS];                 // this lane's logits in split sp
-#pragma unroll
-    for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
-        zs[sp] = zp + ((size_t)min(sp, splits - 1) * T + t) * E + lane;
     float part[SLOTS][RT_MAX_SPLITS], bs[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
@@ -165,7 +300,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
         bs[s] = in ? bias[lane + 64 * s] : 0.f;
 #pragma unroll
         for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
-            part[s][sp] = in ? zs[sp][64 * s] : 0.f;   // splits past the last reread it (unused)
+            part[s][sp] = (in && sp < splits) ? zp[((size_t)sp * T + t) * E + lane + 64 * s] : 0.f;
     }
     uint32_t key[SLOTS];
 #pragma unroll
@@ -176,62 +311,66 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
             if (sp < splits) v += part[s][sp];
         key[s] = (lane + 64 * s < E) ? ordered_bits(v + bs[s]) : 0u;
     }
-    int sel_e[8];
-    float sel_z[8];
+    // tau: the K-th largest image
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (j >= K) { sel_e[j] = 0x7fffffff; sel_z[j] = 0.f; continue; }
-        // this lane's best: largest key, lowest slot on ties
-        uint32_t best = key[0];
-        int bslot = 0;
+        for (int s = 0; s < SLOTS; ++s) cnt += __popcll(__ballot(key[s] >= cand));
+        if (cnt >= K) tau = cand;
+    }
+    // chosen: all images above tau, then images equal to tau by ascending index
+    uint64_t chosen[SLOTS];
+    int need = K;
 #pragma unroll
-        for (int s = 1; s < SLOTS; ++s)
-            if (key[s] > best) { best = key[s]; bslot = s; }
-        const uint32_t m = wave_reduce_u32(best, MaxU32());
-        const uint32_t cand = (best == m) ? (uint32_t)(bslot * 64 + lane) : 0xFFFFFFFFu;
-        const int e = (int)wave_reduce_u32(cand, MinU32());
-        sel_e[j] = e;
-        sel_z[j] = from_ordered_bits(m);
-        if ((e & 63) == lane) {
+    for (int s = 0; s < SLOTS; ++s) {
+        chosen[s] = __ballot(key[s] > tau);
+        need -= __popcll(chosen[s]);
+    }
 #pragma unroll
-            for (int s = 0; s < SLOTS; ++s)
-                if (s == (e >> 6)) key[s] = 0u;
+    for (int s = 0; s < SLOTS; ++s) {
+        uint64_t eq = __ballot(key[s] == tau);
+        while (need > 0 && eq) {
+            const uint64_t low = eq & (~eq + 1);   // lowest set bit
+            chosen[s] |= low;
+            eq ^= low;
+            --need;
         }
     }
-    // canonical order: ascending expert id
+    // output position of each chosen expert: chosen experts of lower slots,
+    // then lower lanes of this slot
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0;
 #pragma unroll
-    for (int a = 1; a < 8; ++a)
-#pragma unroll
-        for (int b = a; b > 0; --b)
-            if (sel_e[b - 1] > sel_e[b]) {
-                int te = sel_e[b - 1]; sel_e[b - 1] = sel_e[b]; sel_e[b] = te;
-                float tz = sel_z[b - 1]; sel_z[b - 1] = sel_z[b]; sel_z[b] = tz;
-            }
-    // weights p_j / sum p.  When every chosen logit is negative the ratios are
-    // formed relative to the largest one so that tiny sigmoids cannot underflow
-    // the sum: sigmoid(a)/sigmoid(m) = e^(a-m) (1+e^m) / (1+e^a).
-    float zmax = sel_z[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j)
-        if (j < K) zmax = fmaxf(zmax, sel_z[j]);
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (j >= K) { p[j] = 0.f; continue; }
-        if (zmax >= 0.f)
-            p[j] = sigmoid_f32(sel_z[j]);
-        else
-            p[j] = expf(sel_z[j] - zmax) * (1.0f + expf(zmax)) / (1.0f + expf(sel_z[j]));
-        psum += p[j];
+    for (int s = 0; s < SLOTS; ++s) {
+        if ((chosen[s] >> lane) & 1ull) {
+            const int j = base + __popcll(chosen[s] & below);
+            sel_e_s[wave][j] = lane + 64 * s;
+            sel_z_s[wave][j] = from_ordered_bits(key[s]);
+        }
+        base += __popcll(chosen[s]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // weights p_j / sum p over the chosen experts in ascending id order.  When
+    // every chosen logit is negative the ratios are formed relative to the
+    // largest one so that tiny sigmoids cannot underflow the sum:
+    // sigmoid(a)/sigmoid(m) = e^(a-m) (1+e^m) / (1+e^a).
+    float zmax = sel_z_s[wave][0];
+    for (int j = 1; j < K; ++j) zmax = fmaxf(zmax, sel_z_s[wave][j]);
+    float psum = 0.f, pl = 0.f;
+    for (int j = 0; j < K; ++j) {
+        const float z = sel_z_s[wave][j];
+        const float pj = (zmax >= 0.f) ? sigmoid_f32(z)
+                                        : expf(z - zmax) * (1.0f + expf(zmax)) / (1.0f + expf(z));
+        psum += pj;
+        if (j == lane) pl = pj;
     }
     if (lane < K) {
-        int e = 0;
-        float pj = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j == lane) { e = sel_e[j]; pj = p[j]; }
-        ids[(size_t)t * K + lane] = e;
-        w[(size_t)t * K + lane] = pj / psum;
+        ids[(size_t)t * K + lane] = sel_e_s[wave][lane];
+        w[(size_t)t * K + lane] = pl / psum;
     }
 }
 
@@ -410,7 +549,16 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
         // workgroups; large: 64-expert blocks
         splits = router_splits(T, D);
         const int n_mt = (T + RT_M - 1) / RT_M;
-        if (T <= 512)
+        if (T >= RL_MIN_T && E <= RL_MAX_E) {
+            const int nfw = ((E + 31) / 32 + 3) / 4;
+            const unsigned g = splits * ((T + 31) / 32);
+            const int ns = router_lds_stages(E);
+            const uint16_t *x = (const uint16_t *)a.x, *wr = (const uint16_t *)a.wr;
+            if (nfw == 1) router_logits_lds_kernel<1><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
+            else if (nfw == 2) router_logits_lds_kernel<2><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
+            else if (nfw == 3) router_logits_lds_kernel<3><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
+            else router_logits_lds_kernel<4><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
+        } else if (T <= 512)
             router_logits_bf16_kernel<1><<<splits * n_mt * ((E + 31) / 32), 256, 0, st>>>(
                 (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z);
         else
@@ -426,7 +574,9 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
         const int g = (T + 3) / 4, slots = (E + 63) / 64;
         if (slots <= 1) topk_kernel<1><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
         else if (slots <= 2) topk_kernel<2><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 3) topk_kernel<3><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
         else if (slots <= 4) topk_kernel<4><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 5) topk_kernel<5><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
         else if (slots <= 8) topk_kernel<8><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
         else topk_kernel<16><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
     }

@@ -35,6 +35,10 @@ SMALL = [
     (103, 67, 192, 24, 8, 64, "f32", "uniform"),
     (104, 130, 64, 16, 8, 64, "bf16", "uniform"),     # minimum widths, heavy load per expert
     (105, 600, 256, 48, 8, 192, "bf16", "zipf"),      # skewed: full, partial and <= 32-row tiles
+    # batches above 512 tokens take the LDS-staged router: ring depth 2 (E=500) and 3 (E=300),
+    # four reduction splits of four 64-wide steps each, ragged token blocks and expert fragments
+    (106, 700, 1024, 500, 8, 64, "bf16", "uniform"),
+    (107, 1000, 1024, 300, 8, 64, "bf16", "zipf"),
 ]
 
 
