@@ -37,7 +37,7 @@ struct RouteWs {
     size_t z, tile_count, tile_base, total;
 };
 struct FfnWs {
-    size_t h, o, sx, list_gu, list_dn, n_items, total;
+    size_t h, o, sx, list_gu, list_dn, n_items, x16, total;
     int bm;
 };
 
@@ -67,7 +67,8 @@ FfnWs ffn_ws(const coli_moe_shape *s, int quant)
     w.list_gu = align_up(w.sx + T * D * 4);
     w.list_dn = align_up(w.list_gu + max_tiles * (size_t)coli::ffn_col_tiles_gu(s->F) * 16);
     w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * 16);
-    w.total = align_up(w.n_items + 20 * 4);
+    w.x16 = align_up(w.n_items + 20 * 4);
+    w.total = quant ? align_up(w.x16 + T * D * 2) : w.x16;
     return w;
 }
 
@@ -289,6 +290,7 @@ coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
     a.list_gu = (int4 *)(base + L.list_gu);
     a.list_dn = (int4 *)(base + L.list_dn);
     a.n_items = (int32_t *)(base + L.n_items);
+    a.x16 = (uint16_t *)(base + L.x16);
     coli::StageMarks marks{events, n_events, 0};
     a.marks = &marks;
     return coli::launch_ffn(a, (hipStream_t)stream) == hipSuccess ? COLI_OK : COLI_E_LAUNCH;

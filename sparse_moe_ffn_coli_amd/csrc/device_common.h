@@ -512,25 +512,40 @@ __device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// fp16 variant of the register-staged engine, for int4 weights
+// int4 engine (fp16 MFMA, fp32 accumulation)
 //
-// Operands are fp16 in LDS and multiplied with v_mfma_f32_32x32x16_f16 (fp32
-// accumulation).  A rows arrive in bf16 and are converted on the way into
-// LDS (exact for magnitudes in fp16's normal range).  Each of the BN (= 256
-// = threads) B rows is staged by one thread, one of two ways per tile:
-//   int4: 32 bytes of nibbles per K step of 64, element 2i in the low nibble
-//         of byte i, value (nibble - 8) * scale with one fp16 scale per
-//         `group` consecutive elements (offset-binary, "feat(glm53): add
-//         device-resident HIP backend for MI350P", section "Key changes");
-//   bf16: converted like the A rows (the shared expert's dense weights).
+// Weights: int4, element 2i in the low nibble of byte i, value (nibble - 8) *
+// scale with one fp16 scale per `group` consecutive elements (offset-binary,
+// "feat(glm53): add device-resident HIP backend for MI350P", section "Key
+// changes"); the shared expert's weights are bf16.  The A operand (token
+// rows of x, or rows of h) is fp16 already, written by the previous kernel
+// in the permuted chunk order described below (exact for magnitudes in
+// fp16's normal range).
 //
-// Both operands are stored with the same order of K inside every 16-byte
-// chunk of 8 elements, 0,4,1,5,2,6,3,7: dword j holds elements j and j + 4.
-// A dot product over the chunk does not depend on that order, and it lets
-// one AND/OR put two nibbles of a 32-bit word (bits 4j and 16 + 4j) under the
-// fp16 exponent of 1024: the pair is then 1024 + n exactly, subtracting 1032
-// leaves n - 8 exactly, and one fp16 multiply by the scale rounds the exact
-// product (n - 8) * scale once, as an fp32 product rounded to fp16 would.
+// Order of K: inside every 8-element chunk the elements are held in the
+// order 0,4,1,5,2,6,3,7 (dword j holds elements j and j + 4).  A dot product
+// does not depend on that order, and it lets one AND/OR put two nibbles of a
+// 32-bit word (bits 4j and 16 + 4j) under the fp16 exponent of 1024: the
+// pair is then 1024 + n exactly, subtracting 1032 leaves n - 8 exactly, and
+// one fp16 multiply by the scale rounds the exact product (n - 8) * scale
+// once.  Inside a 64-element block, lane half h takes elements 32h .. 32h +
+// 31 over four MFMA steps j (chunk 4h + j of A), eight per step: for int4
+// that is exactly the 16-byte chunk 2 blk + h of the weight row's nibbles,
+// one LDS read whose dword j holds the step's nibbles; the 32 elements lie
+// inside one scale group (the group is a multiple of 32).
+//
+// Tile: BM token rows x 256 weight rows, four waves.  One stage covers KS =
+// 128 elements of int4 weights (64 bytes of nibbles per row) or 32 of bf16
+// weights (64 bytes per row as well), so a stage needs 26 KB (BM = 32) or
+// 34 KB (BM = 64) of LDS and two or three workgroups share a CU.  Weight and
+// token rows reach LDS by LDS-DMA copies (16 rows x 64 B or 8 rows x 128 B
+// per instruction); 16-byte chunks are XOR-swizzled so that fragment reads
+// are free of bank conflicts:
+//   B: [256 rows][64 B], chunk ^ (row >> 2) & 3;
+//   A (int4 tiles): [64-element block][BM rows][128 B], chunk ^ (row >> 1) & 7;
+//   A (bf16 tiles): [BM rows][64 B], chunk ^ (row >> 2) & 3;
+// and the stage's scales (at most 4 per weight row) with ordinary loads
+// into S[256][4].
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -549,6 +564,9 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v)
     }
     return r;
 }
+
+// slot of element e (0..7) of a chunk in the order 0,4,1,5,2,6,3,7
+__device__ __forceinline__ int f16_chunk_slot(int e) { return (e & 3) * 2 + (e >> 2); }
 
 // 8 nibbles of w (element p in bits 4p..4p+3) -> 8 fp16 values
 // (nibble - 8) * scale in the chunk order 0,4,1,5,2,6,3,7
@@ -570,106 +588,173 @@ __device__ __forceinline__ f16x2 fp16_bits_splat(uint16_t h)
     return __builtin_bit_cast(f16x2, (uint32_t)h * 0x00010001u);
 }
 
-// ap: A rows (bf16) as in mfma_mainloop.  B row of this thread (row tid):
-// int4 when bq != nullptr (nibbles bq, fp16 scales bs, `group` elements per
-// scale, a multiple of 32), else bf16 row bb.
-template <class C>
-__device__ __forceinline__ void mfma_mainloop_f16(const uint16_t *const (&ap)[C::A_PER_T],
-                                                  const uint16_t *bb, const uint8_t *bq,
-                                                  const uint16_t *bs, int group, int K, uint16_t *lds,
-                                                  f32x16 (&acc)[C::FM][C::FN])
+template <int BM_>
+struct I4Cfg {
+    static constexpr int BM = BM_, BN = 256, NT = 256;
+    static constexpr int WAVES_M = BM / 32, WAVES_N = 4 / WAVES_M;
+    static constexpr int FM = 1, FN = BN / (WAVES_N * 32);
+    static constexpr int KS_I4 = 128, KS_BF = 32;   // reduction elements per stage
+    static constexpr int B_BYTES = BN * 64;
+    static constexpr int A_BYTES = BM * KS_I4 * 2;
+    static constexpr int S_BYTES = BN * 8;
+    static constexpr int STAGE_BYTES = B_BYTES + A_BYTES + S_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int AROWS = BM / 8;            // token rows per lane among the int4 A copy sources
+    static constexpr int WAVES_PER_EU = (BM == 32) ? 3 : 2;   // workgroups per CU that the LDS allows
+    static_assert(BM == 32 || BM == 64, "tile height");
+};
+
+// One tile.  I4: arow[u] is token row 8u + lane / 8 of the tile (element 0),
+// brow[j] weight row (4w + j) * 16 + lane / 4 (byte 0), w = wave, srow the
+// scales of weight row tid.  bf16 tiles: a0 + r * lda is token row r (the
+// shared expert's rows are contiguous), brow as above, srow unused.  valid:
+// token rows of the tile that are real (copies of row groups wholly past
+// them are skipped; their results are dropped by the caller).
+template <class C, bool I4>
+__device__ __forceinline__ void i4_mainloop(const uint16_t *const (&arow)[C::AROWS], const uint16_t *a0,
+                                            int lda, const char *const (&brow)[4], const uint16_t *srow,
+                                            int group, int K, int valid, char *lds, f32x16 (&acc)[C::FN])
 {
-    static_assert(C::BN == C::NT, "one B row per thread");
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int ch0 = tid & 7;
-    const bool i4 = bq != nullptr;
-
-    u32x4 ra[C::A_PER_T];
-    u32x4 rq[2];
-    u32x4 rb[8];
-    f16x2 s0 = {}, s1 = {};
-#define COLI_GLOAD16(kt_)                                                                      \
-    do {                                                                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < C::A_PER_T; ++i_) ra[i_] =                     \
-            *reinterpret_cast<const u32x4 *>(ap[i_] + (kt_) * C::BK);                          \
-        if (i4) {                                                                              \
-            rq[0] = *reinterpret_cast<const u32x4 *>(bq + (kt_) * (C::BK / 2));                \
-            rq[1] = *reinterpret_cast<const u32x4 *>(bq + (kt_) * (C::BK / 2) + 16);           \
-            s0 = fp16_bits_splat(bs[((kt_) * C::BK) / group]);                                   \
-            s1 = fp16_bits_splat(bs[((kt_) * C::BK + 32) / group]);                              \
-        } else {                                                                               \
-            _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rb[j_] =                          \
-                *reinterpret_cast<const u32x4 *>(bb + (kt_) * C::BK + 8 * j_);                 \
-        }                                                                                      \
-    } while (0)
-#define COLI_SSTORE16(buf_)                                                                    \
-    do {                                                                                       \
-        uint16_t *sa_ = lds + (buf_) * C::STAGE;                                               \
-        uint16_t *sb_ = sa_ + C::BM * C::BK;                                                   \
-        _Pragma("unroll") for (int i_ = 0; i_ < C::A_PER_T; ++i_) {                            \
-            const int c_ = tid + i_ * C::NT;                                                   \
-            if (C::A_CHUNKS % C::NT == 0 || c_ < C::A_CHUNKS)                                  \
-                *reinterpret_cast<u32x4 *>(sa_ + swz(c_ >> 3, ch0)) = bf16x8_to_f16x8(ra[i_]); \
-        }                                                                                      \
-        if (i4) {                                                                              \
-            _Pragma("unroll") for (int c_ = 0; c_ < 8; ++c_)                                   \
-                *reinterpret_cast<u32x4 *>(sb_ + swz(tid, c_)) =                               \
-                    int4x8_to_f16x8(rq[c_ >> 2][c_ & 3], c_ < 4 ? s0 : s1);                    \
-        } else {                                                                               \
-            _Pragma("unroll") for (int c_ = 0; c_ < 8; ++c_)                                   \
-                *reinterpret_cast<u32x4 *>(sb_ + swz(tid, c_)) = bf16x8_to_f16x8(rb[c_]);      \
-        }                                                                                      \
-    } while (0)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
+    const int h = lane >> 5;
+    constexpr int KS = I4 ? C::KS_I4 : C::KS_BF;
+    const int nk = (K + KS - 1) / KS;
+    auto dma = [](const void *src, char *dst) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    };
+    // scales of stage kt for weight row tid: groups first .. last.  When the
+    // row's scales fill at most one 128-byte line (group 32, K / 32 a
+    // multiple of 8, at most 64), the whole row is loaded once per tile into
+    // sv and each stage takes its four scales from the front (sv shifts by
+    // one entry every second stage): a scale line is then fetched once per
+    // tile instead of once per stage.
+    uint2 sreg = make_uint2(0u, 0u);
+    const bool sline = I4 && group == 32 && ((K / 32) & 7) == 0 && K / 32 <= 64;
+    u32x4 sv[8];
+    if (sline) {
+        const int n16 = K / 256;                      // 16-byte pieces of the row's scales
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sv[i] = *reinterpret_cast<const u32x4 *>(srow + 8 * min(i, n16 - 1));
+    }
+    auto load_scales = [&](int kt) {
+        if (sline) {
+            sreg = (kt & 1) ? make_uint2(sv[0][2], sv[0][3]) : make_uint2(sv[0][0], sv[0][1]);
+            if (kt & 1) {
+#pragma unroll
+                for (int i = 0; i < 7; ++i) sv[i] = sv[i + 1];
+            }
+            return;
+        }
+        const int first = kt * KS / group, last = (min(K, kt * KS + KS) - 1) / group;
+        const uint32_t s0 = srow[min(first, last)], s1 = srow[min(first + 1, last)];
+        const uint32_t s2 = srow[min(first + 2, last)], s3 = srow[min(first + 3, last)];
+        sreg = make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
+    };
+    auto issue = [&](int kt) {
+        char *sb = lds + (kt & 1) * C::STAGE_BYTES, *sa = sb + C::B_BYTES;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {                 // B: 256 rows of 64 bytes, 16 rows per copy
+            const int q = w * 4 + j;
+            const int row = q * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ ((row >> 2) & 3);
+            if (I4) {
+                const int cs = (kt * KS + 32 * c < K) ? c : 0;      // past K: any valid chunk
+                dma(brow[j] + kt * 64 + cs * 16, sb + q * 1024);
+            } else {
+                dma(brow[j] + (kt * KS + c * 8) * 2, sb + q * 1024);
+            }
+        }
+        if (I4) {                                     // A: lines blk * BM + row of 128 bytes
+            constexpr int AQ = C::BM * 2 / 8;
+#pragma unroll
+            for (int i = 0; i < AQ / 4; ++i) {
+                const int q = w + 4 * i;
+                const int blk = q / C::AROWS, u = q % C::AROWS;
+                if (u * 8 < valid) {
+                    const int row = u * 8 + (lane >> 3);
+                    const int c = (lane & 7) ^ ((row >> 1) & 7);
+                    const int bs = (kt * KS + blk * 64 < K) ? blk : 0;
+                    dma(arow[u] + kt * KS + bs * 64 + c * 8, sa + q * 1024);
+                }
+            }
+            load_scales(kt);
+        } else {                                      // A: BM rows of 64 bytes, 16 rows per copy
+            if (w < C::BM / 16 && w * 16 < valid) {
+                const int row = w * 16 + (lane >> 2);
+                const int c = (lane & 3) ^ ((row >> 2) & 3);
+                dma(a0 + (size_t)min(row, valid - 1) * lda + kt * KS + c * 8, sa + w * 1024);
+            }
+        }
+    };
+    auto store_scales = [&](int kt) {
+        if (I4)
+            *reinterpret_cast<uint2 *>(lds + (kt & 1) * C::STAGE_BYTES + C::B_BYTES + C::A_BYTES + tid * 8) = sreg;
+    };
 
 #pragma unroll
-    for (int m = 0; m < C::FM; ++m)
+    for (int n = 0; n < C::FN; ++n)
 #pragma unroll
-        for (int n = 0; n < C::FN; ++n)
+        for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
+    const int ar = wm * 32 + (lane & 31);             // this lane's A fragment row
+    int br[C::FN];                                    // and B fragment rows
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+    for (int n = 0; n < C::FN; ++n) br[n] = (wn * C::FN + n) * 32 + (lane & 31);
 
-    f16x8 af[2][C::FM], bfr[2][C::FN];
-#define COLI_LFRAG16(stage_, kk_, slot_)                                                       \
-    do {                                                                                       \
-        const uint16_t *sa_ = lds + (stage_) * C::STAGE;                                       \
-        const uint16_t *sb_ = sa_ + C::BM * C::BK;                                             \
-        const int ch_ = (kk_) * 2 + (lane >> 5);                                               \
-        _Pragma("unroll") for (int m_ = 0; m_ < C::FM; ++m_) af[slot_][m_] =                   \
-            *reinterpret_cast<const f16x8 *>(sa_ + swz((wm * C::FM + m_) * 32 + (lane & 31), ch_)); \
-        _Pragma("unroll") for (int n_ = 0; n_ < C::FN; ++n_) bfr[slot_][n_] =                  \
-            *reinterpret_cast<const f16x8 *>(sb_ + swz((wn * C::FN + n_) * 32 + (lane & 31), ch_)); \
-    } while (0)
-
-    const int nk = K / C::BK;
-    COLI_GLOAD16(0);
-    COLI_SSTORE16(0);
+    issue(0);
+    wait_vmcnt_c<0>();
+    store_scales(0);
     __syncthreads();
-    COLI_LFRAG16(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) COLI_GLOAD16(kt + 1);
+        if (kt + 1 < nk) issue(kt + 1);
+        const char *sb = lds + (kt & 1) * C::STAGE_BYTES, *sa = sb + C::B_BYTES;
+        if (I4) {
+            const uint16_t *ss = reinterpret_cast<const uint16_t *>(sa + C::A_BYTES);
+            const int nblk = min(KS / 64, (K - kt * KS) / 64);
+            for (int blk = 0; blk < nblk; ++blk) {
+                const int gi = (kt * KS + 64 * blk + 32 * h) / group - kt * KS / group;
+                u32x4 bq[C::FN];
+                f16x2 sc[C::FN];
 #pragma unroll
-        for (int kk = 0; kk < C::BK / 16; ++kk) {
-            const int slot = kk & 1;
-            if (kk + 1 < C::BK / 16) COLI_LFRAG16(cur, kk + 1, slot ^ 1);
+                for (int n = 0; n < C::FN; ++n) {
+                    const int c = 2 * blk + h;
+                    bq[n] = *reinterpret_cast<const u32x4 *>(sb + br[n] * 64 + ((c ^ ((br[n] >> 2) & 3)) * 16));
+                    sc[n] = fp16_bits_splat(ss[br[n] * 4 + gi]);
+                }
+                f16x8 a[4];
 #pragma unroll
-            for (int m = 0; m < C::FM; ++m)
+                for (int j = 0; j < 4; ++j) {
+                    const int ca = 4 * h + j;
+                    a[j] = *reinterpret_cast<const f16x8 *>(sa + (blk * C::BM + ar) * 128 + ((ca ^ ((ar >> 1) & 7)) * 16));
+                }
 #pragma unroll
-                for (int n = 0; n < C::FN; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[slot][m], bfr[slot][n],
-                                                                       acc[m][n], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int n = 0; n < C::FN; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            a[j], __builtin_bit_cast(f16x8, int4x8_to_f16x8(bq[n][j], sc[n])), acc[n], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = 2 * h + j;
+                const f16x8 a = *reinterpret_cast<const f16x8 *>(sa + ar * 64 + ((c ^ ((ar >> 2) & 3)) * 16));
+#pragma unroll
+                for (int n = 0; n < C::FN; ++n) {
+                    const u32x4 braw = *reinterpret_cast<const u32x4 *>(sb + br[n] * 64 + ((c ^ ((br[n] >> 2) & 3)) * 16));
+                    acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        a, __builtin_bit_cast(f16x8, bf16x8_to_f16x8(braw)), acc[n], 0, 0, 0);
+                }
+            }
         }
         if (kt + 1 < nk) {
-            COLI_SSTORE16(cur ^ 1);
+            wait_vmcnt_c<0>();
+            store_scales(kt + 1);
             __syncthreads();
-            COLI_LFRAG16(cur ^ 1, 0, 0);
         }
     }
-#undef COLI_GLOAD16
-#undef COLI_SSTORE16
-#undef COLI_LFRAG16
 }
 
 }  // namespace coli

@@ -82,13 +82,17 @@ __device__ __forceinline__ WorkTile find_tile(const int32_t *__restrict__ count,
 {
     const int lane = threadIdx.x & 63;
     const int run = (E + 63) >> 6;                 // experts per lane
-    // all counts are loaded at once; each lane keeps the row tiles of its run
+    // all counts are loaded at once (unconditional loads of a clamped index,
+    // so no load waits for another); each lane keeps the row tiles of its run
+    int cnt[FIND_MAX_RUN];
+#pragma unroll
+    for (int k = 0; k < FIND_MAX_RUN; ++k) cnt[k] = count[min(lane * run + k, E - 1)];
     int mtk[FIND_MAX_RUN];
     int local = 0;
 #pragma unroll
     for (int k = 0; k < FIND_MAX_RUN; ++k) {
         const int e = lane * run + k;
-        mtk[k] = (k < run && e < E) ? (count[e] + BM - 1) / BM : 0;
+        mtk[k] = (k < run && e < E) ? (cnt[k] + BM - 1) / BM : 0;
         local += mtk[k];
     }
     int incl = local;
@@ -583,115 +587,136 @@ __global__ __launch_bounds__(512) void down_big_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 1'/2'. int4 routed experts: the same grouped GEMMs on the fp16 engine, the
-// weight rows dequantised while they are staged into LDS.  The shared
-// expert (bf16) shares the gate+up launch: its tiles stage bf16 rows instead.
+// 1'/2'. int4 routed experts: the same grouped GEMMs on the int4 engine
+// (weights dequantised from LDS as their fragments are read).  The shared
+// expert (bf16) shares the launches: its tiles run the engine's bf16 mode.
+// The A operands are fp16 in the engine's chunk order: x16 (written by
+// x_to_f16_kernel) and h16 (written by the gate+up kernel in that order).
 // ---------------------------------------------------------------------------
-template <class C>
-__global__ __launch_bounds__(256) void gateup_int4_kernel(
-    const uint16_t *__restrict__ x, const uint8_t *__restrict__ gate_q, const uint16_t *__restrict__ gate_s,
-    const uint8_t *__restrict__ up_q, const uint16_t *__restrict__ up_s, int group,
-    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restrict__ x, long n8,
+                                                       uint16_t *__restrict__ x16)
 {
-    static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    constexpr int FC = C::BN / 2;
-    const WorkTile item = find_tile(count, E, T, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
-    if (item.e < 0) return;
-    const int nt = item.ct;
-    const int R = T * K;
-    const ExpertTile et = decode_tile(item, count, offset, E, T, R);
-    const int f0 = nt * FC;
-    const int ch0 = threadIdx.x & 7;
-
-    const uint16_t *ap[C::A_PER_T];
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-        int r = et.m0 + a_chunk_row<C>(i);
-        if (a_chunk_row<C>(i) >= C::BM || r >= et.cnt) r = et.m0;
-        const int tok = et.shared ? r : perm[et.base + r] / K;
-        ap[i] = x + (size_t)tok * D + ch0 * 8;
-    }
-    // this thread's B row: block b = row >> 5 holds gate (b even) or up (b odd)
-    const int brow = threadIdx.x, blk = brow >> 5;
-    const int f = min(f0 + (blk >> 1) * 32 + (brow & 31), F - 1);
-    const uint16_t *bb = nullptr;
-    const uint8_t *bq = nullptr;
-    const uint16_t *bs = nullptr;
-    if (et.shared) {
-        bb = ((blk & 1) ? s_up : s_gate) + (size_t)f * D;
-    } else {
-        const size_t row = (size_t)et.e * F + f;
-        bq = ((blk & 1) ? up_q : gate_q) + row * (D / 2);
-        bs = ((blk & 1) ? up_s : gate_s) + row * (D / group);
-    }
-    f32x16 acc[C::FM][C::FN];
-    mfma_mainloop_f16<C>(ap, bb, bq, bs, group, D, lds, acc);
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
-#pragma unroll
-    for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-        for (int n = 0; n < C::FN; n += 2) {
-            const int fo = f0 + ((wn * C::FN + n) >> 1) * 32 + (lane & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
-                if (r < et.cnt && fo < F)
-                    h[(size_t)(et.base + r) * F + fo] =
-                        f32_to_bf16_bits(swiglu_clamped(acc[m][n][i], acc[m][n + 1][i]));
-            }
-        }
+    const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n8) return;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(x + q * 8);
+    *reinterpret_cast<u32x4 *>(x16 + q * 8) = bf16x8_to_f16x8(v);
 }
 
 template <class C>
-__global__ __launch_bounds__(256) void down_int4_kernel(
-    const uint16_t *__restrict__ h, const uint8_t *__restrict__ down_q, const uint16_t *__restrict__ down_s,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU))) void gateup_int4_kernel(
+    const uint16_t *__restrict__ x16, const uint8_t *__restrict__ gate_q, const uint16_t *__restrict__ gate_s,
+    const uint8_t *__restrict__ up_q, const uint16_t *__restrict__ up_s, int group,
+    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
+    const int32_t *__restrict__ perm, int T, int D, int E, int K, int F, uint16_t *__restrict__ h16)
+{
+    static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
+    constexpr int FC = C::BN / 2;
+    const WorkTile item = find_tile(count, E, T, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
+    if (item.e < 0) return;
+    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
+    const int f0 = item.ct * FC;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int valid = min(et.cnt - et.m0, C::BM);
+
+    // weight row tr of the tile: block tr / 32 holds gate (even) or up (odd)
+    // rows f0 + (block / 2) * 32 ..; rows past F read row F - 1
+    auto wrow = [&](int tr) { return min(f0 + ((tr >> 5) >> 1) * 32 + (tr & 31), F - 1); };
+    const char *brow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tr = (w * 4 + j) * 16 + (lane >> 2);
+        const bool upb = (tr >> 5) & 1;
+        brow[j] = et.shared
+            ? reinterpret_cast<const char *>((upb ? s_up : s_gate) + (size_t)wrow(tr) * D)
+            : reinterpret_cast<const char *>((upb ? up_q : gate_q) + ((size_t)et.e * F + wrow(tr)) * (D / 2));
+    }
+    const uint16_t *arow[C::AROWS];
+    f32x16 acc[C::FN];
+    if (et.shared) {
+#pragma unroll
+        for (int u = 0; u < C::AROWS; ++u) arow[u] = x16;
+        i4_mainloop<C, false>(arow, x16 + (size_t)et.m0 * D, D, brow, nullptr, group, D, valid, lds, acc);
+    } else {
+#pragma unroll
+        for (int u = 0; u < C::AROWS; ++u) {
+            int r = et.m0 + u * 8 + (lane >> 3);      // padding rows read the tile's first row
+            if (r >= et.cnt) r = et.m0;
+            arow[u] = x16 + (size_t)(perm[et.base + r] / K) * D;
+        }
+        const int tr = threadIdx.x;
+        const uint16_t *srow = (((tr >> 5) & 1) ? up_s : gate_s) + ((size_t)et.e * F + wrow(tr)) * (D / group);
+        i4_mainloop<C, true>(arow, nullptr, 0, brow, srow, group, D, valid, lds, acc);
+    }
+
+    // h16 in the engine's chunk order: column f is stored at (f & ~7) + slot(f & 7)
+    const int wn = w % C::WAVES_N, wm = w / C::WAVES_N;
+#pragma unroll
+    for (int n = 0; n < C::FN; n += 2) {
+        const int fo = f0 + ((wn * C::FN + n) >> 1) * 32 + (lane & 31);
+        const int fs = (fo & ~7) + f16_chunk_slot(fo & 7);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = et.m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (r < et.cnt && fo < F)
+                h16[(size_t)(et.base + r) * F + fs] =
+                    __builtin_bit_cast(uint16_t, (_Float16)swiglu_clamped(acc[n][i], acc[n + 1][i]));
+        }
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU))) void down_int4_kernel(
+    const uint16_t *__restrict__ h16, const uint8_t *__restrict__ down_q, const uint16_t *__restrict__ down_s,
     int group, const uint16_t *__restrict__ s_down, const int32_t *__restrict__ count,
     const int32_t *__restrict__ offset, int T, int D, int E, int K, int F, uint16_t *__restrict__ o,
     float *__restrict__ sx)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
     const WorkTile item = find_tile(count, E, T, C::BM, (D + TILE_N - 1) / TILE_N);
     if (item.e < 0) return;
     const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
     const int d0 = item.ct * C::BN;
-    const int ch0 = threadIdx.x & 7;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int valid = min(et.cnt - et.m0, C::BM);
 
-    const uint16_t *ap[C::A_PER_T];
+    const char *brow[4];
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-        const int rr = a_chunk_row<C>(i);
-        const int r = (rr < C::BM && et.m0 + rr < et.cnt) ? et.m0 + rr : et.m0;
-        ap[i] = h + (size_t)(et.base + r) * F + ch0 * 8;
+    for (int j = 0; j < 4; ++j) {
+        const int d = min(d0 + (w * 4 + j) * 16 + (lane >> 2), D - 1);
+        brow[j] = et.shared ? reinterpret_cast<const char *>(s_down + (size_t)d * F)
+                            : reinterpret_cast<const char *>(down_q + ((size_t)et.e * D + d) * (F / 2));
     }
-    // this thread's B row: the shared expert's dense bf16 row, else int4
-    const int d = min(d0 + (int)threadIdx.x, D - 1);
-    f32x16 acc[C::FM][C::FN];
+    const uint16_t *arow[C::AROWS];
+    f32x16 acc[C::FN];
     if (et.shared) {
-        mfma_mainloop_f16<C>(ap, s_down + (size_t)d * F, nullptr, nullptr, group, F, lds, acc);
+#pragma unroll
+        for (int u = 0; u < C::AROWS; ++u) arow[u] = h16;
+        i4_mainloop<C, false>(arow, h16 + (size_t)(et.base + et.m0) * F, F, brow, nullptr, group, F, valid, lds,
+                              acc);
     } else {
-        const size_t row = (size_t)et.e * D + d;
-        mfma_mainloop_f16<C>(ap, nullptr, down_q + row * (F / 2), down_s + row * (F / group), group, F, lds,
-                             acc);
+#pragma unroll
+        for (int u = 0; u < C::AROWS; ++u) {
+            int r = et.m0 + u * 8 + (lane >> 3);
+            if (r >= et.cnt) r = et.m0;
+            arow[u] = h16 + (size_t)(et.base + r) * F;
+        }
+        const int d = min(d0 + (int)threadIdx.x, D - 1);
+        i4_mainloop<C, true>(arow, nullptr, 0, brow, down_s + ((size_t)et.e * D + d) * (F / group), group, F,
+                             valid, lds, acc);
     }
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
+    const int wn = w % C::WAVES_N, wm = w / C::WAVES_N;
 #pragma unroll
-    for (int m = 0; m < C::FM; ++m)
+    for (int n = 0; n < C::FN; ++n) {
+        const int dd = d0 + (wn * C::FN + n) * 32 + (lane & 31);
 #pragma unroll
-        for (int n = 0; n < C::FN; ++n) {
-            const int dd = d0 + acc_col<C>(wn, n, lane);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
-                if (r < et.cnt && dd < D) store_down(et, r, dd, D, acc[m][n][i], o, sx);
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int r = et.m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (r < et.cnt && dd < D) store_down(et, r, dd, D, acc[n][i], o, sx);
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -821,9 +846,8 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 // launchers
 // ---------------------------------------------------------------------------
 using SmallCfg = TileCfg<32, 256, 1, 4>;
-using LargeCfg = TileCfg<64, 256, 2, 2>;
 constexpr int BIG_BM = BigCfg::BM;
-static_assert(SmallCfg::BN == TILE_N && LargeCfg::BN == TILE_N && BigCfg::BN == TILE_N,
+static_assert(SmallCfg::BN == TILE_N && I4Cfg<64>::BN == TILE_N && BigCfg::BN == TILE_N,
               "all paths cut columns alike");
 
 int ffn_tile_rows(int T, int E, int K, int int4)
@@ -831,7 +855,7 @@ int ffn_tile_rows(int T, int E, int K, int int4)
     // rows per expert on average decides the tile height
     const long R = (long)T * K;
     if (R <= 24L * E) return SmallCfg::BM;
-    return int4 ? LargeCfg::BM : BIG_BM;
+    return int4 ? I4Cfg<64>::BM : BIG_BM;
 }
 
 long ffn_max_tiles(int T, int E, int K, int bm)
@@ -895,9 +919,11 @@ static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t s
     const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
     const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
+    const long n8 = (long)a.T * a.D / 8;
     mk.mark(st);
+    x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint16_t *)a.x, n8, a.x16);
     gateup_int4_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
-        (const uint16_t *)a.x, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
+        a.x16, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
         (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
@@ -916,9 +942,9 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
     if (a.bf16) {
         if (a.use_int4) {
             if (a.bm == SmallCfg::BM)
-                launch_staged_int4<SmallCfg>(a, mk, st);
+                launch_staged_int4<I4Cfg<32>>(a, mk, st);
             else
-                launch_staged_int4<LargeCfg>(a, mk, st);
+                launch_staged_int4<I4Cfg<64>>(a, mk, st);
         } else if (a.bm == SmallCfg::BM) {
             launch_staged<SmallCfg>(a, mk, st);
         } else {

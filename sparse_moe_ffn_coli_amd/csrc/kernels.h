@@ -50,7 +50,8 @@ struct FfnLaunch {
     const float *residual;
     float *y;
     void *y_bf16;
-    void *h;               // workspace [T*K + T][F]
+    void *h;               // workspace [T*K + T][F] (bf16; fp16 in the int4 engine's chunk order for int4)
+    uint16_t *x16;         // workspace [T][D] (int4 only): x in fp16, the int4 engine's chunk order
     void *o;               // workspace [T*K][D]
     float *sx;             // workspace [T][D] (bf16 path): the shared expert's output
     int4 *list_gu;         // workspace [ffn_max_tiles * ffn_col_tiles_gu] (256-row tiles)
