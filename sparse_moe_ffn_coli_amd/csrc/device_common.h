@@ -569,17 +569,31 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v)
 __device__ __forceinline__ int f16_chunk_slot(int e) { return (e & 3) * 2 + (e >> 2); }
 
 // 8 nibbles of w (element p in bits 4p..4p+3) -> 8 fp16 values
-// (nibble - 8) * scale in the chunk order 0,4,1,5,2,6,3,7
-__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, f16x2 scale2)
+// (nibble - 8) * scale in the chunk order 0,4,1,5,2,6,3,7.  Pairs j = 0, 2
+// take the nibbles from bits 0-3 (and 16-19) of w and of w >> 8: under the
+// exponent of 1024 they read 1024 + n.  Pairs j = 1, 3 take them in place
+// from bits 4-7: 1024 + 16 n, so 1152 is subtracted and the scale divided by
+// 16 (exact: a power of two).  Either way the difference is exact and the
+// one multiply rounds the exact product (n - 8) * scale.  scale16 = scale / 16.
+__device__ __forceinline__ uint32_t nibble_pair(uint32_t w, uint32_t mask, uint32_t magic)
 {
-    const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    // (w & mask) | magic in one instruction (the compiler splits it in two
+    // when both constants are literals); mask in an SGPR, magic in a VGPR
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+    return r;
+}
+__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, f16x2 scale2, f16x2 scale16)
+{
+    const f16x2 off0 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const f16x2 off1 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t w8 = w >> 8;
+    const uint32_t magic = 0x64006400u;
     u32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t d = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-        const f16x2 v = (__builtin_bit_cast(f16x2, d) - off) * scale2;
-        r[j] = __builtin_bit_cast(uint32_t, v);
-    }
+    r[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w, 0x000F000Fu, magic)) - off0) * scale2);
+    r[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w, 0x00F000F0u, magic)) - off1) * scale16);
+    r[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w8, 0x000F000Fu, magic)) - off0) * scale2);
+    r[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w8, 0x00F000F0u, magic)) - off1) * scale16);
     return r;
 }
 
@@ -714,14 +728,17 @@ __device__ __forceinline__ void i4_mainloop(const uint16_t *const (&arow)[C::ARO
             const uint16_t *ss = reinterpret_cast<const uint16_t *>(sa + C::A_BYTES);
             const int nblk = min(KS / 64, (K - kt * KS) / 64);
             for (int blk = 0; blk < nblk; ++blk) {
-                const int gi = (kt * KS + 64 * blk + 32 * h) / group - kt * KS / group;
+                const int gi = (group == 32) ? 2 * blk + h
+                                             : (kt * KS + 64 * blk + 32 * h) / group - kt * KS / group;
                 u32x4 bq[C::FN];
-                f16x2 sc[C::FN];
+                f16x2 sc[C::FN], sc16[C::FN];
+                const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 #pragma unroll
                 for (int n = 0; n < C::FN; ++n) {
                     const int c = 2 * blk + h;
                     bq[n] = *reinterpret_cast<const u32x4 *>(sb + br[n] * 64 + ((c ^ ((br[n] >> 2) & 3)) * 16));
                     sc[n] = fp16_bits_splat(ss[br[n] * 4 + gi]);
+                    sc16[n] = sc[n] * sixteenth;
                 }
                 f16x8 a[4];
 #pragma unroll
@@ -734,7 +751,7 @@ __device__ __forceinline__ void i4_mainloop(const uint16_t *const (&arow)[C::ARO
 #pragma unroll
                     for (int n = 0; n < C::FN; ++n)
                         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            a[j], __builtin_bit_cast(f16x8, int4x8_to_f16x8(bq[n][j], sc[n])), acc[n], 0, 0, 0);
+                            a[j], __builtin_bit_cast(f16x8, int4x8_to_f16x8(bq[n][j], sc[n], sc16[n])), acc[n], 0, 0, 0);
             }
         } else {
 #pragma unroll
