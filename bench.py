@@ -485,7 +485,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if cfg["dtype"] == "f32" else "bf16",
+        "dtype": "f32" if cfg["dtype"] == "f32" else ("fp16 (int4 weights)" if cfg.get("int4") else "bf16"),
         "data": "synthetic (seeded generator, seed 0)",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "global_batch": cfg["T"],
                    "seq_len": 1, "parallelism": "none (one GPU)", "experts": cfg["E"],
