@@ -145,7 +145,10 @@ coli_status coli_moe_ffn(const coli_moe_shape *s, const void *x, const coli_moe_
                          const coli_moe_weights *w, const float *residual, float *y,
                          void *y_bf16, void *ws, size_t ws_bytes, void *stream);
 
-/* As coli_moe_ffn with int4 routed experts (bf16 shapes only). */
+/* As coli_moe_ffn with int4 routed experts (bf16 shapes only).  Arithmetic:
+ * fp16 products with fp32 accumulation -- each weight (nibble - 8) * scale
+ * rounded once to fp16, the activations and the hidden rows of the routed and
+ * shared experts converted to fp16; the combine is as in coli_moe_ffn. */
 coli_status coli_moe_ffn_int4(const coli_moe_shape *s, const void *x,
                               const coli_moe_routing *r, const coli_moe_weights_int4 *w,
                               const float *residual, float *y, void *y_bf16, void *ws,
