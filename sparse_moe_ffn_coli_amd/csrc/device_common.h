@@ -44,6 +44,18 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u)
     return gc / (1.0f + expf(-gc)) * uc;
 }
 
+// The same with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32, about
+// one ulp each), for results that are rounded to bf16 or fp16 right after:
+// a few fp32 ulps are far below that rounding.  Very negative g: the exp2 is
+// +inf, its reciprocal 0, the result -0 (never NaN).
+__device__ __forceinline__ float swiglu_clamped_fast(float g, float u)
+{
+    const float gc = fminf(g, 10.0f);
+    const float uc = fminf(fmaxf(u, -10.0f), 10.0f);
+    const float e = __builtin_amdgcn_exp2f(gc * -1.4426950408889634f);
+    return gc * __builtin_amdgcn_rcpf(1.0f + e) * uc;
+}
+
 // ---------------------------------------------------------------------------
 // Wave-wide reductions on DPP lane permutations (no LDS traffic): within each
 // row of 16 lanes, quad swaps, then the half-row and row mirrors; the four

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(
                 const int r = et.m0 + acc_row<C>(wm, m, lane, i);
                 if (r < et.cnt && f < F)
                     h[(size_t)(et.base + r) * F + f] =
-                        f32_to_bf16_bits(swiglu_clamped(acc[m][n][i], acc[m][n + 1][i]));
+                        f32_to_bf16_bits(swiglu_clamped_fast(acc[m][n][i], acc[m][n + 1][i]));
             }
         }
 }
@@ -425,7 +425,7 @@ __device__ __forceinline__ void gateup_big_body(const uint16_t *const (&rp)[BigC
                 const int r = et.m0 + wm * 64 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                 if (r < et.cnt && f < F)
                     h[(size_t)(et.base + r) * F + f] =
-                        f32_to_bf16_bits(swiglu_clamped(acc[m][n][i], acc[m][n + 1][i]));
+                        f32_to_bf16_bits(swiglu_clamped_fast(acc[m][n][i], acc[m][n + 1][i]));
             }
         }
 }
@@ -473,7 +473,7 @@ __device__ __forceinline__ void gateup_big_tile(
                 const int rr = et.m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                 if (rr < et.cnt && f < F)
                     h[(size_t)(et.base + rr) * F + f] =
-                        f32_to_bf16_bits(swiglu_clamped(acc[n][i], acc[n + 1][i]));
+                        f32_to_bf16_bits(swiglu_clamped_fast(acc[n][i], acc[n + 1][i]));
             }
         }
         return;
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
             const int r = et.m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
             if (r < et.cnt && fo < F)
                 h16[(size_t)(et.base + r) * F + fs] =
-                    __builtin_bit_cast(uint16_t, (_Float16)swiglu_clamped(acc[n][i], acc[n + 1][i]));
+                    __builtin_bit_cast(uint16_t, (_Float16)swiglu_clamped_fast(acc[n][i], acc[n + 1][i]));
         }
     }
 }
