@@ -407,6 +407,46 @@ __device__ __forceinline__ int big_wave_fragments(int rows, int wm)
     return min(max((rows - wm * 64 + 31) >> 5, 0), 2);
 }
 
+// Epilogue of the 256 x 256 down tiles: accumulator element (m, n, i) of a
+// lane is tile row wm * 64 + m * 32 + 8 (i / 4) + 4 (lane / 32) + i % 4 and
+// column 32 n of the lane's column `out` points at; each real row's pointer
+// is formed once and its FN values stored at immediate offsets.  out_row0:
+// the output row of the tile's first row minus et.m0; cols: columns left
+// from the lane's first (fragments at or past it are dropped).
+template <int NFW, class T, class Cvt>
+__device__ __forceinline__ void big_store_rows(const f32x16 (&acc)[BigCfg::FM][BigCfg::FN], const ExpertTile &et,
+                                               T *out, size_t ld, int out_row0, int cols, int w, Cvt cvt)
+{
+    const int lane = threadIdx.x & 63, wm = w >> 1;
+    const int rows = et.cnt - et.m0;
+    const int r0 = wm * 64 + 4 * (lane >> 5);
+    T *const base = out + (size_t)(out_row0 + et.m0) * ld;
+    if (rows >= BigCfg::BM && __builtin_amdgcn_readfirstlane(cols) >= 32 * BigCfg::FN && cols >= 32 * BigCfg::FN) {
+        // every row and column real (a full tile): no checks
+#pragma unroll
+        for (int m = 0; m < NFW; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                T *row = base + (size_t)(r0 + m * 32 + 8 * (i >> 2) + (i & 3)) * ld;
+#pragma unroll
+                for (int n = 0; n < BigCfg::FN; ++n) row[32 * n] = cvt(acc[m][n][i]);
+            }
+        return;
+    }
+#pragma unroll
+    for (int m = 0; m < NFW; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = r0 + m * 32 + 8 * (i >> 2) + (i & 3);
+            if (r < rows) {
+                T *row = base + (size_t)r * ld;
+#pragma unroll
+                for (int n = 0; n < BigCfg::FN; ++n)
+                    if (32 * n < cols) row[32 * n] = cvt(acc[m][n][i]);
+            }
+        }
+}
+
 template <int NFW>
 __device__ __forceinline__ void gateup_big_body(const uint16_t *const (&rp)[BigCfg::CPW], const ExpertTile &et,
                                                 int f0, int D, int F, int w, char *lds,
@@ -415,17 +455,20 @@ __device__ __forceinline__ void gateup_big_body(const uint16_t *const (&rp)[BigC
     f32x16 acc[BigCfg::FM][BigCfg::FN];
     big_mainloop<BigCfg, NFW>(rp, D, min(et.cnt - et.m0, BigCfg::BM), w, lds, acc);
     const int lane = threadIdx.x & 63, wm = w >> 1, wn = w & 1;
+    // fragment pair (n, n + 1) = gate and up of h columns fl + 16 n
+    const int fl = f0 + wn * 64 + (lane & 31);
+    const int rows = et.cnt - et.m0;
+    const int r0 = wm * 64 + 4 * (lane >> 5);
 #pragma unroll
     for (int m = 0; m < NFW; ++m)
 #pragma unroll
-        for (int n = 0; n < BigCfg::FN; n += 2) {
-            const int f = f0 + (wn * 2 + (n >> 1)) * 32 + (lane & 31);
+        for (int i = 0; i < 16; ++i) {
+            const int r = r0 + m * 32 + 8 * (i >> 2) + (i & 3);
+            if (r < rows) {
+                uint16_t *row = h + (size_t)(et.base + et.m0 + r) * F + fl;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = et.m0 + wm * 64 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (r < et.cnt && f < F)
-                    h[(size_t)(et.base + r) * F + f] =
-                        f32_to_bf16_bits(swiglu_clamped_fast(acc[m][n][i], acc[m][n + 1][i]));
+                for (int n = 0; n < BigCfg::FN; n += 2)
+                    if (16 * n < F - fl) row[16 * n] = f32_to_bf16_bits(swiglu_clamped_fast(acc[m][n][i], acc[m][n + 1][i]));
             }
         }
 }
@@ -491,18 +534,10 @@ __device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg
 {
     f32x16 acc[BigCfg::FM][BigCfg::FN];
     big_mainloop<BigCfg, NFW>(rp, F, min(et.cnt - et.m0, BigCfg::BM), w, lds, acc);
-    const int lane = threadIdx.x & 63, wm = w >> 1, wn = w & 1;
-#pragma unroll
-    for (int m = 0; m < NFW; ++m)
-#pragma unroll
-        for (int n = 0; n < BigCfg::FN; ++n) {
-            const int d = d0 + (wn * BigCfg::FN + n) * 32 + (lane & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = et.m0 + wm * 64 + m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (r < et.cnt && d < D) store_down(et, r, d, D, acc[m][n][i], o, sx);
-            }
-        }
+    const int lane = threadIdx.x & 63, wn = w & 1;
+    const int dl = d0 + wn * BigCfg::FN * 32 + (lane & 31);   // column of fragment n: dl + 32 n
+    if (et.shared) big_store_rows<NFW>(acc, et, sx + dl, (size_t)D, 0, D - dl, w, [](float v) { return v; });
+    else big_store_rows<NFW>(acc, et, o + dl, (size_t)D, et.base, D - dl, w, [](float v) { return f32_to_bf16_bits(v); });
 }
 
 __device__ __forceinline__ void down_big_tile(
