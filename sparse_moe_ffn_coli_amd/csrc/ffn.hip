@@ -283,6 +283,33 @@ __device__ __forceinline__ const uint16_t *gateup_b_row(const uint16_t *G, const
     return ((blk & 1) ? U : G) + (size_t)f * D;
 }
 
+// Epilogue of the grouped kernels: accumulator element (m, n, i) of a lane is
+// tile row r0 + 32 m + 8 (i / 4) + i % 4 (r0 = the lane's first row: its
+// wave's first row + 4 (lane / 32)) and column 32 n of the lane's column
+// `out` points at.  Each real row's pointer is formed once and the FN values
+// stored at immediate offsets.  out_row0: output row of the tile's row 0
+// minus et.m0; cols: columns left from the lane's first (later fragments
+// are dropped); val(m, n, i): the value to store.
+template <int FM, int FN, class T, class Val>
+__device__ __forceinline__ void frag_store_rows(const ExpertTile &et, T *out, size_t ld, int out_row0, int r0,
+                                                int cols, Val val)
+{
+    const int rows = et.cnt - et.m0;
+    T *const base = out + (size_t)(out_row0 + et.m0) * ld;
+#pragma unroll
+    for (int m = 0; m < FM; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = r0 + 32 * m + 8 * (i >> 2) + (i & 3);
+            if (r < rows) {
+                T *row = base + (size_t)r * ld;
+#pragma unroll
+                for (int n = 0; n < FN; ++n)
+                    if (32 * n < cols) row[32 * n] = val(m, n, i);
+            }
+        }
+}
+
 // ---------------------------------------------------------------------------
 // 1. gate+up grouped GEMM with the clamped SwiGLU in the epilogue, h in bf16.
 // ---------------------------------------------------------------------------
@@ -323,31 +350,19 @@ __global__ __launch_bounds__(256) void gateup_kernel(
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
-#pragma unroll
-    for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-        for (int n = 0; n < C::FN; n += 2) {
-            const int f = f0 + ((wn * C::FN + n) >> 1) * 32 + (lane & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
-                if (r < et.cnt && f < F)
-                    h[(size_t)(et.base + r) * F + f] =
-                        f32_to_bf16_bits(swiglu_clamped_fast(acc[m][n][i], acc[m][n + 1][i]));
-            }
-        }
+    // fragment pair (2p, 2p + 1) = gate and up of h columns fl + 32 p
+    const int fl = f0 + wn * (C::FN / 2) * 32 + (lane & 31);
+    frag_store_rows<C::FM, C::FN / 2>(et, h + fl, (size_t)F, et.base, wm * C::FM * 32 + 4 * (lane >> 5), F - fl,
+                                      [&](int m, int p, int i) {
+                                          return f32_to_bf16_bits(
+                                              swiglu_clamped_fast(acc[m][2 * p][i], acc[m][2 * p + 1][i]));
+                                      });
 }
 
 // ---------------------------------------------------------------------------
 // 2. down grouped GEMM: o[row] = W_down[e] h[row] in bf16 for the routed rows,
 //    sx[t] = S_down h[R + t] in fp32 for the shared expert's rows.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_down(const ExpertTile &et, int r, int d, int D, float v,
-                                           uint16_t *__restrict__ o, float *__restrict__ sx)
-{
-    if (et.shared) sx[(size_t)r * D + d] = v;
-    else o[(size_t)(et.base + r) * D + d] = f32_to_bf16_bits(v);
-}
 
 template <class C>
 __global__ __launch_bounds__(256) void down_kernel(
@@ -382,17 +397,14 @@ __global__ __launch_bounds__(256) void down_kernel(
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
-#pragma unroll
-    for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-        for (int n = 0; n < C::FN; ++n) {
-            const int d = d0 + acc_col<C>(wn, n, lane);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = et.m0 + acc_row<C>(wm, m, lane, i);
-                if (r < et.cnt && d < D) store_down(et, r, d, D, acc[m][n][i], o, sx);
-            }
-        }
+    const int dl = d0 + acc_col<C>(wn, 0, lane);
+    const int r0 = wm * C::FM * 32 + 4 * (lane >> 5);
+    if (et.shared)
+        frag_store_rows<C::FM, C::FN>(et, sx + dl, (size_t)D, 0, r0, D - dl,
+                                      [&](int m, int n, int i) { return acc[m][n][i]; });
+    else
+        frag_store_rows<C::FM, C::FN>(et, o + dl, (size_t)D, et.base, r0, D - dl,
+                                      [&](int m, int n, int i) { return f32_to_bf16_bits(acc[m][n][i]); });
 }
 
 // ---------------------------------------------------------------------------
@@ -507,18 +519,12 @@ __device__ __forceinline__ void gateup_big_tile(
         f32x16 acc[4];
         stream_mainloop(ra, rb, D, w, lds, acc);
         if ((w >> 1) != 0) return;
-        const int lane = threadIdx.x & 63, wn = w & 1;
-#pragma unroll
-        for (int n = 0; n < 4; n += 2) {
-            const int f = f0 + (wn * 2 + (n >> 1)) * 32 + (lane & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int rr = et.m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (rr < et.cnt && f < F)
-                    h[(size_t)(et.base + rr) * F + f] =
-                        f32_to_bf16_bits(swiglu_clamped_fast(acc[n][i], acc[n + 1][i]));
-            }
-        }
+        // fragment pair (2p, 2p + 1) = gate and up of h columns fl + 32 p
+        const int fl = f0 + (w & 1) * 64 + (threadIdx.x & 31);
+        frag_store_rows<1, 2>(et, h + fl, (size_t)F, et.base, 4 * ((threadIdx.x & 63) >> 5), F - fl,
+                              [&](int, int p, int i) {
+                                  return f32_to_bf16_bits(swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
+                              });
         return;
     }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
@@ -570,16 +576,13 @@ __device__ __forceinline__ void down_big_tile(
         f32x16 acc[4];
         stream_mainloop(ra, rb, F, w, lds, acc);
         if ((w >> 1) != 0) return;
-        const int lane = threadIdx.x & 63, wn = w & 1;
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int d = d0 + (wn * 4 + n) * 32 + (lane & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int rr = et.m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (rr < et.cnt && d < D) store_down(et, rr, d, D, acc[n][i], o, sx);
-            }
-        }
+        const int dl = d0 + (w & 1) * 128 + (threadIdx.x & 31);
+        if (et.shared)
+            frag_store_rows<1, 4>(et, sx + dl, (size_t)D, 0, 4 * ((threadIdx.x & 63) >> 5), D - dl,
+                                  [&](int, int n, int i) { return acc[n][i]; });
+        else
+            frag_store_rows<1, 4>(et, o + dl, (size_t)D, et.base, 4 * ((threadIdx.x & 63) >> 5), D - dl,
+                                  [&](int, int n, int i) { return f32_to_bf16_bits(acc[n][i]); });
         return;
     }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
@@ -686,19 +689,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
     }
 
     // h16 in the engine's chunk order: column f is stored at (f & ~7) + slot(f & 7)
+    // (fragment pair (2p, 2p + 1) = columns fo + 32 p; 32 p keeps the chunk slot)
     const int wn = w % C::WAVES_N, wm = w / C::WAVES_N;
-#pragma unroll
-    for (int n = 0; n < C::FN; n += 2) {
-        const int fo = f0 + ((wn * C::FN + n) >> 1) * 32 + (lane & 31);
-        const int fs = (fo & ~7) + f16_chunk_slot(fo & 7);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = et.m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (r < et.cnt && fo < F)
-                h16[(size_t)(et.base + r) * F + fs] =
-                    __builtin_bit_cast(uint16_t, (_Float16)swiglu_clamped_fast(acc[n][i], acc[n + 1][i]));
-        }
-    }
+    const int fo = f0 + wn * (C::FN / 2) * 32 + (lane & 31);
+    const int fs = (fo & ~7) + f16_chunk_slot(fo & 7);
+    frag_store_rows<1, C::FN / 2>(et, h16 + fs, (size_t)F, et.base, wm * 32 + 4 * (lane >> 5), F - fo,
+                                  [&](int, int p, int i) {
+                                      return __builtin_bit_cast(
+                                          uint16_t, (_Float16)swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
+                                  });
 }
 
 template <class C>
@@ -743,15 +742,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
     }
 
     const int wn = w % C::WAVES_N, wm = w / C::WAVES_N;
-#pragma unroll
-    for (int n = 0; n < C::FN; ++n) {
-        const int dd = d0 + (wn * C::FN + n) * 32 + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = et.m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (r < et.cnt && dd < D) store_down(et, r, dd, D, acc[n][i], o, sx);
-        }
-    }
+    const int dl = d0 + wn * C::FN * 32 + (lane & 31);
+    const int r0 = wm * 32 + 4 * (lane >> 5);
+    if (et.shared)
+        frag_store_rows<1, C::FN>(et, sx + dl, (size_t)D, 0, r0, D - dl, [&](int, int n, int i) { return acc[n][i]; });
+    else
+        frag_store_rows<1, C::FN>(et, o + dl, (size_t)D, et.base, r0, D - dl,
+                                  [&](int, int n, int i) { return f32_to_bf16_bits(acc[n][i]); });
 }
 
 // ---------------------------------------------------------------------------
