@@ -81,7 +81,9 @@ typedef struct {
  *   ids    [T][K] int32  the chosen experts of each token, ascending
  *   w      [T][K] fp32   their routing weights (sum to one per token)
  *   count  [E]    int32  tokens routed to each expert
- *   offset [E+1]  int32  exclusive prefix sums of count (offset[E] = T*K)
+ *   offset [E+1]  int32  exclusive prefix sums of count (offset[E] = T*K); the
+ *                        FFN entry points derive the same sums from count and
+ *                        do not read it
  *   perm   [T*K]  int32  row -> t*K + j; rows grouped by expert ascending,
  *                        tokens ascending within an expert (stable sort)
  *   inv    [T*K]  int32  t*K + j -> row (inverse of perm) */

@@ -224,7 +224,7 @@ coli_status coli_moe_ffn_timed(const coli_moe_shape *s, const void *x, const col
     a.bf16 = s->dtype == COLI_BF16;
     a.bm = L.bm;
     a.x = x;
-    a.ids = r->ids; a.w = r->w; a.count = r->count; a.offset = r->offset; a.perm = r->perm;
+    a.ids = r->ids; a.w = r->w; a.count = r->count; a.perm = r->perm;
     a.inv = r->inv;
     a.gate = w->gate; a.up = w->up; a.down = w->down;
     a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
@@ -276,7 +276,7 @@ coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
     a.bf16 = true;
     a.bm = L.bm;
     a.x = x;
-    a.ids = r->ids; a.w = r->w; a.count = r->count; a.offset = r->offset; a.perm = r->perm;
+    a.ids = r->ids; a.w = r->w; a.count = r->count; a.perm = r->perm;
     a.inv = r->inv;
     a.use_int4 = true;
     a.gate_q = w->gate_q; a.up_q = w->up_q; a.down_q = w->down_q;

@@ -72,59 +72,78 @@ __device__ __forceinline__ int xcd_tile(int ntiles)
 
 static long xcd_grid(long max_items) { return ((max_items + 7) / 8) * 8; }
 
-struct WorkTile {
-    int e, m0, ct;          // expert (E: the shared one), first row, column tile; e < 0: no tile
+// A tile of a grouped kernel: expert e (E: the shared expert; e < 0: no
+// tile), its first row m0, column tile ct, the expert's row count and the
+// expert's first row in the h / o buffers.
+struct ExpertTile {
+    int e, m0, ct, cnt, base;
+    bool shared;
 };
 
 constexpr int FIND_MAX_RUN = 16;     // experts per lane for E <= 1024
 
-__device__ __forceinline__ WorkTile find_tile(const int32_t *__restrict__ count, int E, int T, int BM, int nnt)
+// Tile of this block for BM-row tiles and nnt column tiles.  The expert's row
+// count and first row come from the same register copy of the counts as the
+// search (the first row of expert e is the sum of the counts before it), so
+// the tile is known after one round of loads.  R = T * K routed rows.
+__device__ __forceinline__ ExpertTile find_tile(const int32_t *__restrict__ count, int E, int T, int R, int BM,
+                                                int nnt)
 {
     const int lane = threadIdx.x & 63;
     const int run = (E + 63) >> 6;                 // experts per lane
     // all counts are loaded at once (unconditional loads of a clamped index,
-    // so no load waits for another); each lane keeps the row tiles of its run
+    // so no load waits for another); each lane keeps the counts and row
+    // tiles of its run
     int cnt[FIND_MAX_RUN];
 #pragma unroll
     for (int k = 0; k < FIND_MAX_RUN; ++k) cnt[k] = count[min(lane * run + k, E - 1)];
     int mtk[FIND_MAX_RUN];
-    int local = 0;
+    int local = 0, clocal = 0;
 #pragma unroll
     for (int k = 0; k < FIND_MAX_RUN; ++k) {
         const int e = lane * run + k;
-        mtk[k] = (k < run && e < E) ? (cnt[k] + BM - 1) / BM : 0;
+        if (!(k < run && e < E)) cnt[k] = 0;
+        mtk[k] = (cnt[k] + BM - 1) / BM;
         local += mtk[k];
+        clocal += cnt[k];
     }
-    int incl = local;
+    int incl = local, cincl = clocal;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
+        const int v = __shfl_up(incl, off), c = __shfl_up(cincl, off);
+        if (lane >= off) {
+            incl += v;
+            cincl += c;
+        }
     }
     const int routed = __shfl(incl, 63);
     const int mt_sh = (T + BM - 1) / BM;
     const int t = xcd_tile((routed + mt_sh) * nnt);
-    if (t < 0) return WorkTile{-1, 0, 0};
+    if (t < 0) return ExpertTile{-1, 0, 0, 0, 0, false};
     const int i = t / nnt;                         // row tile index over all experts
-    int e = E, mte = mt_sh, first = routed;
+    int e = E, mte = mt_sh, first = routed, ecnt = T, base = R;
     if (i < routed) {
-        const int L = __builtin_ctzll(__ballot(incl > i));   // first lane whose run ends past i
-        first = __shfl(incl - local, L);
-        // walk lane L's run with its register copies (the loop bounds are
-        // uniform, so every lane takes part in each shuffle)
+        // first lane whose run ends past i (uniform, so its registers are
+        // read with readlane)
+        const int L = __builtin_ctzll(__ballot(incl > i));
+        first = __builtin_amdgcn_readlane(incl - local, L);
+        base = __builtin_amdgcn_readlane(cincl - clocal, L);
 #pragma unroll
         for (int k = 0; k < FIND_MAX_RUN; ++k) {
-            const int m = __shfl(mtk[k], L);
+            const int m = __builtin_amdgcn_readlane(mtk[k], L);
+            const int c = __builtin_amdgcn_readlane(cnt[k], L);
             if (first + m > i) {
                 e = L * run + k;
                 mte = m;
+                ecnt = c;
                 break;
             }
             first += m;
+            base += c;
         }
     }
     const int2 mn = block_order(t - first * nnt, mte, nnt);
-    return WorkTile{e, mn.x * BM, mn.y};
+    return ExpertTile{e, mn.x * BM, mn.y, ecnt, base, e == E};
 }
 
 // The 256 x 256 kernels run one workgroup per CU, so nothing hides a
@@ -180,15 +199,17 @@ constexpr int TILES_LDS_ROWS = 4096;     // row tiles with an owner entry in LDS
 constexpr int TILES_LDS_COST = 8192;     // entries per list with a cost in LDS
 
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
-                                                         int BM, int nnt_gu, int nnt_dn,
+                                                         int R, int BM, int nnt_gu, int nnt_dn,
                                                          int4 *__restrict__ list_gu,
                                                          int4 *__restrict__ list_dn,
                                                          int32_t *__restrict__ n_items)
 {
     // cnt[e]: rows of expert e; sc[e] = row tiles of routed experts 0..e
-    // (inclusive scan); the shared expert's ceil(T/BM) row tiles follow them
+    // (inclusive scan); the shared expert's ceil(T/BM) row tiles follow them;
+    // first[e]: first row of expert e in h / o (exclusive scan of the counts)
     __shared__ int32_t cnt[1024];
     __shared__ int32_t sc[1024];
+    __shared__ int32_t first_s[1024];
     __shared__ int32_t ws[16];
     __shared__ int16_t owner_s[TILES_LDS_ROWS];
     __shared__ int16_t cost_gu[TILES_LDS_COST], cost_dn[TILES_LDS_COST];
@@ -198,13 +219,16 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
     const int mte_t = (c + BM - 1) / BM;
     sc[tid] = block_scan_incl_1024(mte_t, ws);
     __syncthreads();
+    first_s[tid] = block_scan_incl_1024(c, ws) - c;
+    __syncthreads();
     const int routed = sc[1023];
     const int mt_sh = (T + BM - 1) / BM;
     const bool table = routed <= TILES_LDS_ROWS;
     if (table && tid < E)
         for (int i = sc[tid] - mte_t; i < sc[tid]; ++i) owner_s[i] = (int16_t)tid;
     __syncthreads();
-    // entry q of a list with nnt column tiles -> (expert, first row, column tile)
+    // entry q of a list with nnt column tiles -> {expert | column tile << 16,
+    // first row, rows of the expert, first row of the expert in h / o}
     auto entry = [&](int q, int nnt) {
         const int i = q / nnt;
         int e = E;
@@ -223,12 +247,10 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
         const int mte = (e == E) ? mt_sh : (cnt[e] + BM - 1) / BM;
         const int first = (e == E) ? routed : sc[e] - mte;
         const int2 mn = block_order(q - first * nnt, mte, nnt);
-        return make_int4(e, mn.x * BM, mn.y, 0);
+        return (e == E) ? make_int4(e | (mn.y << 16), mn.x * BM, T, R)
+                        : make_int4(e | (mn.y << 16), mn.x * BM, cnt[e], first_s[e]);
     };
-    auto cost_of = [&](const int4 &en) {
-        const int rows = (en.x == E) ? T : cnt[en.x];
-        return TILE_COST0 + min(BM, rows - en.y);
-    };
+    auto cost_of = [&](const int4 &en) { return TILE_COST0 + min(BM, en.z - en.y); };
     const int n_gu = (routed + mt_sh) * nnt_gu, n_dn = (routed + mt_sh) * nnt_dn;
     for (int q = tid; q < n_gu; q += 1024) {
         const int4 en = entry(q, nnt_gu);
@@ -251,24 +273,11 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
               n_items + 2 + 9);
 }
 
-// ---------------------------------------------------------------------------
-// Tile decode shared by the grouped kernels
-// ---------------------------------------------------------------------------
-struct ExpertTile {
-    int e, m0, cnt, base;   // expert, first row, rows of the expert, first row in h/o
-    bool shared;
-};
-
-__device__ __forceinline__ ExpertTile decode_tile(const WorkTile &wt, const int32_t *count,
-                                                  const int32_t *offset, int E, int T, int R)
+// List entry of the 256 x 256 kernels: {e | ct << 16, m0, cnt, base}.
+__device__ __forceinline__ ExpertTile list_tile(const int4 &en, int E)
 {
-    ExpertTile r;
-    r.e = wt.e;
-    r.m0 = wt.m0;
-    r.shared = (wt.e == E);
-    r.cnt = r.shared ? T : count[wt.e];
-    r.base = r.shared ? R : offset[wt.e];
-    return r;
+    const int e = en.x & 0xffff;
+    return ExpertTile{e, en.y, en.x >> 16, en.z, en.w, e == E};
 }
 
 // Gate/up B rows are interleaved in blocks of 32: block b of a 2*FC-row tile
@@ -317,17 +326,15 @@ template <class C>
 __global__ __launch_bounds__(256) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+    const int32_t *__restrict__ count, const int32_t *__restrict__ perm, int T, int D, int E, int K, int F,
+    uint16_t *__restrict__ h)
 {
     static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
     constexpr int FC = C::BN / 2;                 // output columns per tile
-    const WorkTile item = find_tile(count, E, T, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
-    if (item.e < 0) return;
-    const int nt = item.ct;
-    const int R = T * K;
-    const ExpertTile et = decode_tile(item, count, offset, E, T, R);
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
+    if (et.e < 0) return;
+    const int nt = et.ct;
     const uint16_t *G = et.shared ? s_gate : gate + (size_t)et.e * F * D;
     const uint16_t *U = et.shared ? s_up : up + (size_t)et.e * F * D;
     const int f0 = nt * FC;
@@ -340,7 +347,11 @@ __global__ __launch_bounds__(256) void gateup_kernel(
         // padding rows (past the expert's last row) reread its first row
         int r = et.m0 + a_chunk_row<C>(i);
         if (a_chunk_row<C>(i) >= C::BM || r >= et.cnt) r = et.m0;
-        const int tok = et.shared ? r : perm[et.base + r] / K;
+        // every lane loads (a clamped index for the shared expert) and the
+        // value is selected, not branched on, so the loads of all rows are
+        // in flight together
+        const int p = perm[min(et.base + r, T * K - 1)];
+        const int tok = (et.shared ? r * K : p) / K;
         ap[i] = x + (size_t)tok * D + ch0 * 8;
     }
 #pragma unroll
@@ -367,16 +378,14 @@ __global__ __launch_bounds__(256) void gateup_kernel(
 template <class C>
 __global__ __launch_bounds__(256) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    int T, int D, int E, int K, int F,
+    const int32_t *__restrict__ count, int T, int D, int E, int K, int F,
     uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const WorkTile item = find_tile(count, E, T, C::BM, (D + TILE_N - 1) / TILE_N);
-    if (item.e < 0) return;
-    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (D + TILE_N - 1) / TILE_N);
+    if (et.e < 0) return;
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
-    const int d0 = item.ct * C::BN;                    // the last column tile may be ragged
+    const int d0 = et.ct * C::BN;                    // the last column tile may be ragged
     const int ch0 = threadIdx.x & 7;
 
     const uint16_t *ap[C::A_PER_T];
@@ -486,18 +495,14 @@ __device__ __forceinline__ void gateup_big_body(const uint16_t *const (&rp)[BigC
 }
 
 __device__ __forceinline__ void gateup_big_tile(
-    int t, const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
-    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, const int4 *__restrict__ list, int T, int D, int E, int K, int F,
-    char *lds, uint16_t *__restrict__ h)
+    const ExpertTile &et, const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate,
+    const uint16_t *__restrict__ up, const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
+    const int32_t *__restrict__ perm, int T, int D, int K, int F, char *lds, uint16_t *__restrict__ h)
 {
-    const int4 entry = list[t];
-    const WorkTile item{entry.x, entry.y, entry.z};
-    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
+    const int R = T * K;
     const uint16_t *G = et.shared ? s_gate : gate + (size_t)et.e * F * D;
     const uint16_t *U = et.shared ? s_up : up + (size_t)et.e * F * D;
-    const int f0 = item.ct * (BigCfg::BN / 2);
+    const int f0 = et.ct * (BigCfg::BN / 2);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint16_t *rp[BigCfg::CPW];
 #pragma unroll
@@ -506,14 +511,19 @@ __device__ __forceinline__ void gateup_big_tile(
         const int ch = big_copy_chunk<BigCfg>(row);
         int r = et.m0 + row;                      // padding rows reread the tile's first row
         if (r >= et.cnt) r = et.m0;
-        const int tok = et.shared ? r : perm[et.base + r] / K;
+        // every lane loads (a clamped index for the shared expert) and the
+        // value is selected, not branched on, so the loads of all rows are
+        // in flight together
+        const int p = perm[min(et.base + r, R - 1)];
+        const int tok = (et.shared ? r * K : p) / K;
         rp[j] = x + (size_t)tok * D + ch * 8;
         rp[BigCfg::CPO + j] = gateup_b_row(G, U, f0, row, D, F) + ch * 8;
     }
     if (et.cnt - et.m0 <= 32) {
         const int row = stream_a_row(w);
         const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
-        const int tok = et.shared ? r : perm[et.base + r] / K;
+        const int p = perm[min(et.base + r, R - 1)];
+        const int tok = (et.shared ? r * K : p) / K;
         const uint16_t *ra = x + (size_t)tok * D + big_copy_chunk<BigCfg>(row) * 8;
         const uint16_t *rb[4] = {rp[BigCfg::CPO], rp[BigCfg::CPO + 1], rp[BigCfg::CPO + 2], rp[BigCfg::CPO + 3]};
         f32x16 acc[4];
@@ -547,14 +557,11 @@ __device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg
 }
 
 __device__ __forceinline__ void down_big_tile(
-    int t, const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset, const int4 *__restrict__ list,
-    int T, int D, int E, int K, int F, char *lds, uint16_t *__restrict__ o, float *__restrict__ sx)
+    const ExpertTile &et, const uint16_t *__restrict__ h, const uint16_t *__restrict__ down,
+    const uint16_t *__restrict__ s_down, int D, int F, char *lds, uint16_t *__restrict__ o,
+    float *__restrict__ sx)
 {
-    const int4 entry = list[t];
-    const WorkTile item{entry.x, entry.y, entry.z};
-    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
-    const int d0 = item.ct * BigCfg::BN;
+    const int d0 = et.ct * BigCfg::BN;
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint16_t *rp[BigCfg::CPW];
@@ -591,36 +598,44 @@ __device__ __forceinline__ void down_big_tile(
     else down_big_body<0>(rp, et, d0, D, F, w, lds, o, sx);
 }
 
+// Between two tiles of a workgroup: every wave has finished reading LDS
+// (its LDS reads have returned) before any wave's copies of the next tile
+// overwrite it.  The epilogue's global stores need not have completed, so
+// this is a bare barrier rather than __syncthreads(), which also waits for
+// them.
+__device__ __forceinline__ void tile_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Workgroup (x = blockIdx % 8, its XCD) walks range x of the list with a
-// stride of gridDim / 8 workgroups; the barrier ends each tile's use of LDS.
+// stride of gridDim / 8 workgroups.
 __global__ __launch_bounds__(512) void gateup_big_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up,
-    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, const int4 *__restrict__ list, const int32_t *__restrict__ n_items,
-    int T, int D, int E, int K, int F, uint16_t *__restrict__ h)
+    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up, const int32_t *__restrict__ perm,
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int K, int F,
+    uint16_t *__restrict__ h)
 {
     __shared__ __attribute__((aligned(1024))) char lds[BIG_LDS_BYTES];
     const int xc = blockIdx.x & 7;
     const int beg = max(n_items[2 + xc], 0), end = min(n_items[2 + xc + 1], n_items[1]);
     for (int t = beg + (blockIdx.x >> 3); t < end; t += gridDim.x >> 3) {
-        gateup_big_tile(t, x, gate, up, s_gate, s_up, count, offset, perm, list, T, D, E, K, F, lds, h);
-        __syncthreads();
+        gateup_big_tile(list_tile(list[t], E), x, gate, up, s_gate, s_up, perm, T, D, K, F, lds, h);
+        tile_barrier();
     }
 }
 
 __global__ __launch_bounds__(512) void down_big_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int K, int F,
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int E, int F,
     uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(1024))) char lds[BIG_LDS_BYTES];
     const int xc = blockIdx.x & 7;
     const int beg = max(n_items[11 + xc], 0), end = min(n_items[11 + xc + 1], n_items[0]);
     for (int t = beg + (blockIdx.x >> 3); t < end; t += gridDim.x >> 3) {
-        down_big_tile(t, h, down, s_down, count, offset, list, T, D, E, K, F, lds, o, sx);
-        __syncthreads();
+        down_big_tile(list_tile(list[t], E), h, down, s_down, D, F, lds, o, sx);
+        tile_barrier();
     }
 }
 
@@ -645,16 +660,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
     const uint16_t *__restrict__ x16, const uint8_t *__restrict__ gate_q, const uint16_t *__restrict__ gate_s,
     const uint8_t *__restrict__ up_q, const uint16_t *__restrict__ up_s, int group,
     const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
-    const int32_t *__restrict__ count, const int32_t *__restrict__ offset,
-    const int32_t *__restrict__ perm, int T, int D, int E, int K, int F, uint16_t *__restrict__ h16)
+    const int32_t *__restrict__ count, const int32_t *__restrict__ perm, int T, int D, int E, int K, int F,
+    uint16_t *__restrict__ h16)
 {
     static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
     constexpr int FC = C::BN / 2;
-    const WorkTile item = find_tile(count, E, T, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
-    if (item.e < 0) return;
-    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
-    const int f0 = item.ct * FC;
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
+    if (et.e < 0) return;
+    const int f0 = et.ct * FC;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int valid = min(et.cnt - et.m0, C::BM);
 
@@ -703,15 +717,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
 template <class C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU))) void down_int4_kernel(
     const uint16_t *__restrict__ h16, const uint8_t *__restrict__ down_q, const uint16_t *__restrict__ down_s,
-    int group, const uint16_t *__restrict__ s_down, const int32_t *__restrict__ count,
-    const int32_t *__restrict__ offset, int T, int D, int E, int K, int F, uint16_t *__restrict__ o,
-    float *__restrict__ sx)
+    int group, const uint16_t *__restrict__ s_down, const int32_t *__restrict__ count, int T, int D, int E, int K,
+    int F, uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
-    const WorkTile item = find_tile(count, E, T, C::BM, (D + TILE_N - 1) / TILE_N);
-    if (item.e < 0) return;
-    const ExpertTile et = decode_tile(item, count, offset, E, T, T * K);
-    const int d0 = item.ct * C::BN;
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (D + TILE_N - 1) / TILE_N);
+    if (et.e < 0) return;
+    const int d0 = et.ct * C::BN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int valid = min(et.cnt - et.m0, C::BM);
 
@@ -917,11 +929,11 @@ static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     mk.mark(st);
     gateup_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
-        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm,
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.perm,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
-        (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count, a.offset,
+        (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
@@ -932,16 +944,16 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
     const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     mk.mark(st);
-    ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, a.T, BigCfg::BM, ffn_col_tiles_gu(a.F),
+    ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, a.T, a.T * a.K, BigCfg::BM, ffn_col_tiles_gu(a.F),
                                          ffn_col_tiles_dn(a.D), a.list_gu, a.list_dn, a.n_items);
     gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
-        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm, a.list_gu,
-        a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.perm, a.list_gu, a.n_items,
+        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_big_kernel<<<(unsigned)grid_dn, BigCfg::NT, 0, st>>>(
-        (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count, a.offset,
-        a.list_dn, a.n_items, a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
+        (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.list_dn,
+        a.n_items, a.D, a.E, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 
@@ -956,11 +968,11 @@ static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t s
     x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint16_t *)a.x, n8, a.x16);
     gateup_int4_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         a.x16, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
-        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.offset, a.perm,
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.perm,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
     down_int4_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
-        (const uint16_t *)a.h, a.down_q, a.down_s, a.group, (const uint16_t *)a.s_down, a.count, a.offset,
+        (const uint16_t *)a.h, a.down_q, a.down_s, a.group, (const uint16_t *)a.s_down, a.count,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }

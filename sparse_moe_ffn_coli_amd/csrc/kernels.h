@@ -41,7 +41,7 @@ struct FfnLaunch {
     const void *x;
     const int32_t *ids;
     const float *w;
-    const int32_t *count, *offset, *perm, *inv;
+    const int32_t *count, *perm, *inv;
     const void *gate, *up, *down, *s_gate, *s_up, *s_down;
     bool use_int4;         // routed experts in int4 (then gate/up/down above are unused)
     const uint8_t *gate_q, *up_q, *down_q;
