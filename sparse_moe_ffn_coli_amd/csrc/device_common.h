@@ -407,6 +407,40 @@ __device__ __forceinline__ void big_mainloop(const uint16_t *const (&rp)[C::CPW]
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
         if (s < nk) COLI_BIG_ISSUE(s);
+    if constexpr (C::NS >= 3) {
+        // With three or more stages the barrier of step kt comes before its
+        // last MFMA group and also covers stage kt + 1 (issued two steps
+        // earlier): its first fragments are then read while the last MFMAs
+        // of stage kt run, so no step starts by waiting for LDS reads.
+        constexpr int KK = C::BK / 16;
+        big_wait_stages<C, C::NS - 2>(min(C::NS - 2, nk - 1));
+        asm volatile("s_barrier" ::: "memory");
+        if (NFW > 0) COLI_BIG_LFRAG(lds, 0, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const char *st = lds + (kt % C::NS) * C::STAGE_BYTES;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int slot = kk & 1;          // KK is even: stage kt + 1 starts in slot 0
+                if (kk + 1 < KK) {
+                    if (NFW > 0) COLI_BIG_LFRAG(st, kk + 1, slot ^ 1);
+                } else {
+                    // stages issued after kt + 1 that may still be in flight
+                    big_wait_stages<C, C::NS - 3>(max(min(C::NS - 3, nk - 2 - kt), 0));
+                    asm volatile("s_barrier" ::: "memory");
+                    if (kt + C::NS - 1 < nk) COLI_BIG_ISSUE(kt + C::NS - 1);
+                    if (NFW > 0 && kt + 1 < nk)
+                        COLI_BIG_LFRAG(lds + ((kt + 1) % C::NS) * C::STAGE_BYTES, 0, slot ^ 1);
+                }
+#pragma unroll
+                for (int m = 0; m < NFW; ++m)
+#pragma unroll
+                    for (int n = 0; n < C::FN; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][m], bfr[slot][n],
+                                                                            acc[m][n], 0, 0, 0);
+            }
+        }
+        return;
+    }
     for (int kt = 0; kt < nk; ++kt) {
         // stages issued after kt that may still be in flight
         big_wait_stages<C, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));

@@ -45,14 +45,26 @@ namespace coli {
 constexpr int ROW_BLOCK = 8;
 constexpr int TILE_N = 256;          // columns of a tile in every bf16/int4 grouped kernel
 
+// q / d for 0 <= q, d < 2^22 without an integer division (whose expansion
+// is several times longer): the float quotient from the hardware
+// reciprocal is within one of the exact one and is corrected.
+__device__ __forceinline__ int small_div(int q, int d)
+{
+    int i = (int)((float)q * __builtin_amdgcn_rcpf((float)d));
+    if (i * d > q) --i;
+    else if ((i + 1) * d <= q) ++i;
+    return i;
+}
+
 // Tile `local` of an expert with `mte` row tiles and `nnt` column tiles ->
 // (row tile, column tile) in the block order described above.
 __device__ __forceinline__ int2 block_order(int local, int mte, int nnt)
 {
     const int per_block = ROW_BLOCK * nnt;
-    const int blk = local / per_block, in = local % per_block;
+    const int blk = small_div(local, per_block), in = local - blk * per_block;
     const int rows = min(ROW_BLOCK, mte - blk * ROW_BLOCK);   // the last block may be short
-    return make_int2(blk * ROW_BLOCK + in % rows, in / rows);
+    const int ct = small_div(in, rows);
+    return make_int2(blk * ROW_BLOCK + in - ct * rows, ct);
 }
 
 // XCD-aware block -> tile map.  Workgroups are dispatched to the 8 XCDs
@@ -169,15 +181,25 @@ __device__ __forceinline__ void xcd_split(int n, Cost &&cost, int32_t *__restric
     for (int q = q0; q < q1; ++q) c += cost(q);
     csum[tid] = block_scan_incl_1024(c, ws);
     __syncthreads();
-    const long total = csum[1023];
-    const long tot = max(total, 1L);
+    const long tot = max((long)csum[1023], 1L);
+    // floor(8 b / tot) >= x  <=>  b >= ceil(x tot / 8): the XCD of a cost
+    // prefix b is the number of these thresholds it reaches (x = 1..7)
+    long thr[8];
+#pragma unroll
+    for (int x = 1; x < 8; ++x) thr[x] = (x * tot + 7) >> 3;
+    auto xcd_of = [&](long b) {
+        int xq = 0;
+#pragma unroll
+        for (int x = 1; x < 8; ++x) xq += (b >= thr[x]) ? 1 : 0;
+        return xq;
+    };
     long before = csum[tid] - c;                  // cost of entries before q0
     // XCD of entry q0 - 1 (-1 for the first entry), so that a boundary on
     // this chunk's first entry is written by this thread
     int prev = -1;
-    if (q0 > 0 && q0 < n) prev = (int)min(7L, (before - cost(q0 - 1)) * 8 / tot);
+    if (q0 > 0 && q0 < n) prev = xcd_of(before - cost(q0 - 1));
     for (int q = q0; q < q1; ++q) {
-        const int xq = (int)min(7L, before * 8 / tot);
+        const int xq = xcd_of(before);
         for (int xx = prev + 1; xx <= xq; ++xx) starts[xx] = q;    // first entry of XCD xx
         prev = xq;
         before += cost(q);
@@ -199,7 +221,7 @@ constexpr int TILES_LDS_ROWS = 4096;     // row tiles with an owner entry in LDS
 constexpr int TILES_LDS_COST = 8192;     // entries per list with a cost in LDS
 
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
-                                                         int R, int BM, int nnt_gu, int nnt_dn,
+                                                         int R, int nnt_gu, int nnt_dn,
                                                          int4 *__restrict__ list_gu,
                                                          int4 *__restrict__ list_dn,
                                                          int32_t *__restrict__ n_items)
@@ -213,6 +235,7 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
     __shared__ int32_t ws[16];
     __shared__ int16_t owner_s[TILES_LDS_ROWS];
     __shared__ int16_t cost_gu[TILES_LDS_COST], cost_dn[TILES_LDS_COST];
+    constexpr int BM = BigCfg::BM;
     const int tid = threadIdx.x;
     const int c = (tid < E) ? count[tid] : 0;
     cnt[tid] = c;
@@ -230,7 +253,7 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
     // entry q of a list with nnt column tiles -> {expert | column tile << 16,
     // first row, rows of the expert, first row of the expert in h / o}
     auto entry = [&](int q, int nnt) {
-        const int i = q / nnt;
+        const int i = small_div(q, nnt);
         int e = E;
         if (i < routed) {
             if (table) {
@@ -423,6 +446,7 @@ __global__ __launch_bounds__(256) void down_kernel(
 // fragments.
 // ---------------------------------------------------------------------------
 constexpr int BIG_LDS_BYTES = (BigCfg::LDS_BYTES > StreamCfg::LDS_BYTES) ? BigCfg::LDS_BYTES : StreamCfg::LDS_BYTES;
+using StreamRows = BigCfgT<64, 2>;                // copy layout of the streaming mode's rows
 __device__ __forceinline__ int big_wave_fragments(int rows, int wm)
 {
     return min(max((rows - wm * 64 + 31) >> 5, 0), 2);
@@ -504,28 +528,21 @@ __device__ __forceinline__ void gateup_big_tile(
     const uint16_t *U = et.shared ? s_up : up + (size_t)et.e * F * D;
     const int f0 = et.ct * (BigCfg::BN / 2);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint16_t *rp[BigCfg::CPW];
-#pragma unroll
-    for (int j = 0; j < BigCfg::CPO; ++j) {
-        const int row = big_copy_row<BigCfg>(j, w);
-        const int ch = big_copy_chunk<BigCfg>(row);
-        int r = et.m0 + row;                      // padding rows reread the tile's first row
-        if (r >= et.cnt) r = et.m0;
-        // every lane loads (a clamped index for the shared expert) and the
-        // value is selected, not branched on, so the loads of all rows are
-        // in flight together
-        const int p = perm[min(et.base + r, R - 1)];
-        const int tok = (et.shared ? r * K : p) / K;
-        rp[j] = x + (size_t)tok * D + ch * 8;
-        rp[BigCfg::CPO + j] = gateup_b_row(G, U, f0, row, D, F) + ch * 8;
-    }
     if (et.cnt - et.m0 <= 32) {
+        using S = StreamRows;
         const int row = stream_a_row(w);
         const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
+        // every lane loads (a clamped index for the shared expert) and the
+        // value is selected, not branched on, so no load waits for another
         const int p = perm[min(et.base + r, R - 1)];
         const int tok = (et.shared ? r * K : p) / K;
-        const uint16_t *ra = x + (size_t)tok * D + big_copy_chunk<BigCfg>(row) * 8;
-        const uint16_t *rb[4] = {rp[BigCfg::CPO], rp[BigCfg::CPO + 1], rp[BigCfg::CPO + 2], rp[BigCfg::CPO + 3]};
+        const uint16_t *ra = x + (size_t)tok * D + big_copy_chunk<S>(row) * 8;
+        const uint16_t *rb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int br = big_copy_row<S>(j, w);
+            rb[j] = gateup_b_row(G, U, f0, br, D, F) + big_copy_chunk<S>(br) * 8;
+        }
         f32x16 acc[4];
         stream_mainloop(ra, rb, D, w, lds, acc);
         if ((w >> 1) != 0) return;
@@ -536,6 +553,18 @@ __device__ __forceinline__ void gateup_big_tile(
                                   return f32_to_bf16_bits(swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
                               });
         return;
+    }
+    const uint16_t *rp[BigCfg::CPW];
+#pragma unroll
+    for (int j = 0; j < BigCfg::CPO; ++j) {
+        const int row = big_copy_row<BigCfg>(j, w);
+        const int ch = big_copy_chunk<BigCfg>(row);
+        int r = et.m0 + row;                      // padding rows reread the tile's first row
+        if (r >= et.cnt) r = et.m0;
+        const int p = perm[min(et.base + r, R - 1)];
+        const int tok = (et.shared ? r * K : p) / K;
+        rp[j] = x + (size_t)tok * D + ch * 8;
+        rp[BigCfg::CPO + j] = gateup_b_row(G, U, f0, row, D, F) + ch * 8;
     }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
     if (nfw == 2) gateup_big_body<2>(rp, et, f0, D, F, w, lds, h);
@@ -564,22 +593,17 @@ __device__ __forceinline__ void down_big_tile(
     const int d0 = et.ct * BigCfg::BN;
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint16_t *rp[BigCfg::CPW];
-#pragma unroll
-    for (int j = 0; j < BigCfg::CPO; ++j) {
-        const int row = big_copy_row<BigCfg>(j, w);
-        const int ch = big_copy_chunk<BigCfg>(row);
-        int r = et.m0 + row;
-        if (r >= et.cnt) r = et.m0;
-        rp[j] = h + (size_t)(et.base + r) * F + ch * 8;
-        const int d = min(d0 + row, D - 1);       // rows past D reread the last one
-        rp[BigCfg::CPO + j] = W + (size_t)d * F + ch * 8;
-    }
     if (et.cnt - et.m0 <= 32) {
+        using S = StreamRows;
         const int row = stream_a_row(w);
         const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
-        const uint16_t *ra = h + (size_t)(et.base + r) * F + big_copy_chunk<BigCfg>(row) * 8;
-        const uint16_t *rb[4] = {rp[BigCfg::CPO], rp[BigCfg::CPO + 1], rp[BigCfg::CPO + 2], rp[BigCfg::CPO + 3]};
+        const uint16_t *ra = h + (size_t)(et.base + r) * F + big_copy_chunk<S>(row) * 8;
+        const uint16_t *rb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int br = big_copy_row<S>(j, w);
+            rb[j] = W + (size_t)min(d0 + br, D - 1) * F + big_copy_chunk<S>(br) * 8;
+        }
         f32x16 acc[4];
         stream_mainloop(ra, rb, F, w, lds, acc);
         if ((w >> 1) != 0) return;
@@ -591,6 +615,17 @@ __device__ __forceinline__ void down_big_tile(
             frag_store_rows<1, 4>(et, o + dl, (size_t)D, et.base, 4 * ((threadIdx.x & 63) >> 5), D - dl,
                                   [&](int, int n, int i) { return f32_to_bf16_bits(acc[n][i]); });
         return;
+    }
+    const uint16_t *rp[BigCfg::CPW];
+#pragma unroll
+    for (int j = 0; j < BigCfg::CPO; ++j) {
+        const int row = big_copy_row<BigCfg>(j, w);
+        const int ch = big_copy_chunk<BigCfg>(row);
+        int r = et.m0 + row;
+        if (r >= et.cnt) r = et.m0;
+        rp[j] = h + (size_t)(et.base + r) * F + ch * 8;
+        const int d = min(d0 + row, D - 1);       // rows past D reread the last one
+        rp[BigCfg::CPO + j] = W + (size_t)d * F + ch * 8;
     }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
     if (nfw == 2) down_big_body<2>(rp, et, d0, D, F, w, lds, o, sx);
@@ -944,7 +979,7 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
     const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     mk.mark(st);
-    ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, a.T, a.T * a.K, BigCfg::BM, ffn_col_tiles_gu(a.F),
+    ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, a.T, a.T * a.K, ffn_col_tiles_gu(a.F),
                                          ffn_col_tiles_dn(a.D), a.list_gu, a.list_dn, a.n_items);
     gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
