@@ -34,7 +34,7 @@ coli_status check_shape(const coli_moe_shape *s)
 }
 
 struct RouteWs {
-    size_t z, tile_count, tile_base, total;
+    size_t z, tile_count, total;
 };
 struct FfnWs {
     size_t h, o, sx, list_gu, list_dn, n_items, x16, total;
@@ -48,8 +48,7 @@ RouteWs route_ws(const coli_moe_shape *s)
     const size_t ntiles = (size_t)coli::perm_tiles(s->T);
     w.z = 0;
     w.tile_count = align_up(w.z + (size_t)coli::router_splits(s->T, s->D) * T * E * 4);
-    w.tile_base = align_up(w.tile_count + ntiles * E * 4);
-    w.total = align_up(w.tile_base + ntiles * E * 4);
+    w.total = align_up(w.tile_count + ntiles * E * 4);
     return w;
 }
 
@@ -165,7 +164,6 @@ coli_status coli_moe_route_timed(const coli_moe_shape *s, const void *x, const v
     char *base = (char *)ws;
     a.z = (float *)(base + L.z);
     a.tile_count = (int32_t *)(base + L.tile_count);
-    a.tile_base = (int32_t *)(base + L.tile_base);
     a.ids = out->ids; a.w = out->w; a.count = out->count; a.offset = out->offset;
     a.perm = out->perm; a.inv = out->inv;
     coli::StageMarks marks{events, n_events, 0};

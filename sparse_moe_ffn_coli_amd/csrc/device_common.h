@@ -77,11 +77,12 @@ struct MaxU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { r
 struct MinU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
 
 // ---------------------------------------------------------------------------
-// Inclusive prefix sum over the 1024 threads of a workgroup (thread order):
-// a shuffle scan inside each wave, then one wave scans the 16 wave totals.
-// Two barriers; `ws` is 16 ints of LDS.  Every thread must call it.
+// Inclusive prefix sum over the NW waves of a workgroup (thread order):
+// a shuffle scan inside each wave, then one wave scans the NW wave totals.
+// Two barriers; `ws` is NW ints of LDS.  Every thread must call it.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int block_scan_incl_1024(int v, int32_t *ws)
+template <int NW>
+__device__ __forceinline__ int block_scan_incl(int v, int32_t *ws)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -92,17 +93,18 @@ __device__ __forceinline__ int block_scan_incl_1024(int v, int32_t *ws)
     if (lane == 63) ws[wave] = v;
     __syncthreads();
     if (wave == 0) {
-        int w = (lane < 16) ? ws[lane] : 0;
+        int w = (lane < NW) ? ws[lane] : 0;
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
+        for (int off = 1; off < NW; off <<= 1) {
             const int u = __shfl_up(w, off);
             if (lane >= off) w += u;
         }
-        if (lane < 16) ws[lane] = w;
+        if (lane < NW) ws[lane] = w;
     }
     __syncthreads();
     return v + (wave > 0 ? ws[wave - 1] : 0);
 }
+__device__ __forceinline__ int block_scan_incl_1024(int v, int32_t *ws) { return block_scan_incl<16>(v, ws); }
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA tile engine

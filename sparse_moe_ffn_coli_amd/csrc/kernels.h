@@ -27,7 +27,6 @@ struct RouteLaunch {
     const float *bias;
     float *z;              // workspace [router_splits][T][E]: partial logits
     int32_t *tile_count;   // workspace [perm_tiles(T)][E]
-    int32_t *tile_base;    // workspace [perm_tiles(T)][E]
     int32_t *ids;
     float *w;
     int32_t *count, *offset, *perm, *inv;

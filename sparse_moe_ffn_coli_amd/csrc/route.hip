@@ -101,31 +101,41 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// router logits, bf16 inputs, large batches.  One workgroup per (32-token
-// block, reduction split) covers every expert, so each token row is fetched
-// once per split and the router matrix is shared by all token blocks from
-// L2.  Each 64-wide reduction step copies the block's 32 token rows and the
-// E router rows (padded to 32) global -> LDS, eight 128-byte rows per copy
-// instruction, through a ring of up to RL_MAX_STAGES stages (as many as fit
-// in LDS).  Rows are XOR-swizzled in 16-byte chunks so the fragment reads
-// are free of bank conflicts.  Wave w computes expert fragments w, w+4, ...
-// over the whole split; split s's partial sums go to zp[s][t][e] (top-K adds
-// the splits in order and then the bias).
+// router logits, bf16 inputs, large batches.  One workgroup of 8 waves per
+// (64-token block, reduction split) covers every expert, so each token row is
+// fetched once per split and the router matrix is shared by all token blocks
+// from L2.  Each 64-wide reduction step needs the block's 64 token rows and
+// the E router rows (padded to 32), copied global -> LDS eight 128-byte rows
+// per copy instruction into two rings: token-row slots of 8 KB with XS - 1
+// steps issued ahead, router-row slots with WS - 1 steps in flight.  Each
+// wave waits for its own copies of step kt's router rows (the token rows of
+// step kt were issued before them, and copies complete in order), then the
+// barrier makes everyone's visible.  Rows are XOR-swizzled in 16-byte chunks
+// so the fragment reads are free of bank conflicts.  Wave w computes tokens
+// 32 (w / 4) .. +31 of the block against expert fragments w % 4, w % 4 + 4,
+// ... over the whole split (two waves per SIMD hide each other's LDS and
+// MFMA latencies); split s's partial sums go to zp[s][t][e] (top-K adds the
+// splits in order and then the bias).
 // ---------------------------------------------------------------------------
 constexpr int RL_BK = 64;
 constexpr int RL_MAX_E = 512;
-constexpr int RL_MAX_STAGES = 4;
 constexpr int RL_LDS_BYTES = 160 * 1024;
 constexpr int RL_MIN_T = 513;       // smaller batches use the register-streamed kernel above
+constexpr int RL_TOK = 64;          // tokens per workgroup
+constexpr int RL_XSLOT = RL_TOK * 128;
+constexpr int RL_MAX_XS = 6;        // token-row slots
 
-// Stages of the ring for E experts (the stage holds 32 + E rounded up to 32 rows).
-static int router_lds_stages(int E)
+// Ring sizes for E experts: `ws` router-row slots (3, else 2) of
+// ceil(E / 32) * 4 KB, then as many token-row slots as fit, at most RL_MAX_XS.
+static void router_lds_rings(int E, int *xs, int *ws)
 {
-    const int stage = (32 + (E + 31) / 32 * 32) * 128;
-    return std::min(RL_MAX_STAGES, RL_LDS_BYTES / stage);
+    const int wstage = (E + 31) / 32 * 4096;
+    *ws = (3 * wstage + RL_MAX_XS * RL_XSLOT <= RL_LDS_BYTES) ? 3 : 2;
+    *xs = std::min(RL_MAX_XS, (RL_LDS_BYTES - *ws * wstage) / RL_XSLOT);
 }
 
-// s_waitcnt needs an immediate: wave-uniform n in [0, 63] via a jump table.
+// s_waitcnt needs an immediate: wave-uniform n in [0, 39] via a jump table
+// (a larger n waits for every copy, which is also correct).
 __device__ __forceinline__ void wait_vmcnt_rt(int n)
 {
     switch (n) {
@@ -134,80 +144,117 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n)
         COLI_VM(8) COLI_VM(9) COLI_VM(10) COLI_VM(11) COLI_VM(12) COLI_VM(13) COLI_VM(14) COLI_VM(15)
         COLI_VM(16) COLI_VM(17) COLI_VM(18) COLI_VM(19) COLI_VM(20) COLI_VM(21) COLI_VM(22) COLI_VM(23)
         COLI_VM(24) COLI_VM(25) COLI_VM(26) COLI_VM(27) COLI_VM(28) COLI_VM(29) COLI_VM(30) COLI_VM(31)
-        COLI_VM(32) COLI_VM(33) COLI_VM(34) COLI_VM(35)
+        COLI_VM(32) COLI_VM(33) COLI_VM(34) COLI_VM(35) COLI_VM(36) COLI_VM(37) COLI_VM(38) COLI_VM(39)
 #undef COLI_VM
         default: wait_vmcnt_c<0>(); break;
     }
 }
 
 template <int NFW>                    // expert fragments per wave: nfrag <= 4 * NFW
-__global__ __launch_bounds__(256) void router_logits_lds_kernel(
+__global__ __launch_bounds__(512) void router_logits_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int D, int E, int splits,
-    int ns, float *__restrict__ zp)
+    int xs, int ws, float *__restrict__ zp)
 {
-    constexpr int CPW_MAX = 1 + 4 * NFW;
+    constexpr int CPW_MAX = 2 * NFW;              // router-row copies per wave per step
     __shared__ __attribute__((aligned(1024))) char lds[RL_LDS_BYTES];
     const int nfrag = (E + 31) / 32;
-    const int rows = 32 + nfrag * 32;             // LDS rows per stage: tokens, then experts
-    const int stage_bytes = rows * 128;
-    const int cpw = rows / 32;                    // copy instructions per wave per stage (same for all waves)
-    const int n_mt = (T + 31) / 32;
+    const int wstage = nfrag * 4096;              // router rows of one step
+    char *const xl = lds;                         // token-row slots
+    char *const wl = lds + xs * RL_XSLOT;         // router-row slots
+    const int n_mt = (T + RL_TOK - 1) / RL_TOK;
     const int sp = blockIdx.x / n_mt, mt = blockIdx.x % n_mt;
-    const int t0 = mt * 32;
+    const int t0 = mt * RL_TOK;
     const int kq = D / splits, nk = kq / RL_BK;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int th = w >> 2, wc = w & 3;            // token half, expert fragment column
 
-    // copy j of wave w fills LDS rows (w + 4j) * 8 .. +7; lane l takes row
-    // (w + 4j) * 8 + l / 8, whose chunk position l % 8 holds the row's global
-    // chunk (l % 8) ^ ((row / 2) % 8).  Rows past T or E reread a valid row.
-    const uint16_t *src[CPW_MAX];
+    // a copy fills 8 LDS rows; lane l takes row 8 c + l / 8, whose chunk
+    // position l % 8 holds the row's global chunk (l % 8) ^ ((row / 2) % 8).
+    // Wave w copies token rows 8 w .. 8 w + 7 and router-row groups q = w + 8 j
+    // (rows 8 q .. 8 q + 7) for q < 4 nfrag; rows past T or E reread a valid row.
+    const int xr = w * 8 + (lane >> 3);
+    const uint16_t *xsrc = x + (size_t)min(t0 + xr, T - 1) * D + (size_t)sp * kq + ((lane & 7) ^ ((xr >> 1) & 7)) * 8;
+    const int cw = max(0, (4 * nfrag - w + 7) / 8);   // this wave's router-row copies per step
+    const uint16_t *wsrc[CPW_MAX];
 #pragma unroll
     for (int j = 0; j < CPW_MAX; ++j) {
-        const int r = min((w + 4 * j) * 8, rows - 8) + (lane >> 3);
-        src[j] = ((r < 32) ? x + (size_t)min(t0 + r, T - 1) * D : wr + (size_t)min(r - 32, E - 1) * D)
-                 + (size_t)sp * kq + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+        const int r = (w + 8 * j) * 8 + (lane >> 3);
+        wsrc[j] = wr + (size_t)min(r, E - 1) * D + (size_t)sp * kq + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
     }
     // the workgroups start their reduction at different steps (rot), so the
     // ones running together read different columns of the shared router rows
     const int rot = mt % nk;
-    auto issue = [&](int s) {
-        char *st = lds + (s % ns) * stage_bytes;
-        const int kb = (s + rot < nk) ? s + rot : s + rot - nk;
+    auto kblock = [&](int s) { return (s + rot < nk) ? s + rot : s + rot - nk; };
+    auto issue_x = [&](int s) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(xsrc + kblock(s) * RL_BK),
+                                         (__attribute__((address_space(3))) void *)(xl + (s % xs) * RL_XSLOT + w * 1024),
+                                         16, 0, 0);
+    };
+    auto issue_w = [&](int s) {
+        char *st = wl + (s % ws) * wstage;
+        const int kb = kblock(s);
 #pragma unroll
         for (int j = 0; j < CPW_MAX; ++j)
-            if (j < cpw)
+            if (j < cw)
                 __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(src[j] + kb * RL_BK),
-                    (__attribute__((address_space(3))) void *)(st + (w + 4 * j) * 1024), 16, 0, 0);
+                    (const __attribute__((address_space(1))) void *)(wsrc[j] + kb * RL_BK),
+                    (__attribute__((address_space(3))) void *)(st + (w + 8 * j) * 1024), 16, 0, 0);
     };
 
-    // fragment i of wave w: experts (w + 4i) * 32 ..; past the last fragment
-    // the wave recomputes the last one and drops the result
+    // fragment i of wave w: experts (w % 4 + 4i) * 32 ..; past the last
+    // fragment the wave recomputes the last one and drops the result
+    const int arow = th * 32 + (lane & 31);
     int brow[NFW];
 #pragma unroll
-    for (int i = 0; i < NFW; ++i) brow[i] = 32 + min(w + 4 * i, nfrag - 1) * 32 + (lane & 31);
+    for (int i = 0; i < NFW; ++i) brow[i] = min(wc + 4 * i, nfrag - 1) * 32 + (lane & 31);
     f32x16 acc[NFW];
 #pragma unroll
     for (int i = 0; i < NFW; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
 
-    for (int s = 0; s < min(ns - 1, nk); ++s) issue(s);
+    // issued: this wave's copy instructions so far; f0, f1: its count right
+    // after the router rows of the oldest (next) steps in flight were issued
+    const int xa = xs - 1;
+    int issued = 0, f0 = 0, f1 = 0;
+    for (int s = 0; s < min(xa, nk); ++s) {
+        issue_x(s);
+        ++issued;
+    }
+    issue_w(0);
+    issued += cw;
+    f0 = issued;
+    if (ws == 3 && nk > 1) {
+        issue_w(1);
+        issued += cw;
+        f1 = issued;
+    }
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vmcnt_rt(min(ns - 2, nk - 1 - kt) * cpw);      // this wave's copies of stage kt landed
-        asm volatile("s_barrier" ::: "memory");             // everyone's; stage kt-1 fully read
-        if (kt + ns - 1 < nk) issue(kt + ns - 1);
-        const char *st = lds + (kt % ns) * stage_bytes;
+        wait_vmcnt_rt(issued - f0);                 // this wave's copies of step kt landed
+        f0 = f1;
+        asm volatile("s_barrier" ::: "memory");     // everyone's; step kt-1 fully read
+        if (kt + xa < nk) {
+            issue_x(kt + xa);
+            ++issued;
+        }
+        if (kt + ws - 1 < nk) {
+            issue_w(kt + ws - 1);
+            issued += cw;
+            if (ws == 3) f1 = issued;
+            else f0 = issued;
+        }
+        const char *xst = xl + (kt % xs) * RL_XSLOT;
+        const char *wst = wl + (kt % ws) * wstage;
         bf16x8 a[RL_BK / 16], b[RL_BK / 16][NFW];
 #pragma unroll
         for (int kk = 0; kk < RL_BK / 16; ++kk) {
             const int c = kk * 2 + (lane >> 5);
-            a[kk] = *reinterpret_cast<const bf16x8 *>(st + swz(lane & 31, c) * 2);
+            a[kk] = *reinterpret_cast<const bf16x8 *>(xst + swz(arow, c) * 2);
 #pragma unroll
-            for (int i = 0; i < NFW; ++i) b[kk][i] = *reinterpret_cast<const bf16x8 *>(st + swz(brow[i], c) * 2);
+            for (int i = 0; i < NFW; ++i) b[kk][i] = *reinterpret_cast<const bf16x8 *>(wst + swz(brow[i], c) * 2);
         }
-        __builtin_amdgcn_sched_barrier(0);   // all of the stage's fragment reads in flight before its MFMAs
+        __builtin_amdgcn_sched_barrier(0);   // all of the step's fragment reads in flight before its MFMAs
 #pragma unroll
         for (int kk = 0; kk < RL_BK / 16; ++kk)
 #pragma unroll
@@ -217,12 +264,12 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(
     float *z = zp + (size_t)sp * T * E;
 #pragma unroll
     for (int i = 0; i < NFW; ++i) {
-        const int f = w + 4 * i;
+        const int f = wc + 4 * i;
         if (f >= nfrag) continue;
         const int e = f * 32 + (lane & 31);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int t = t0 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            const int t = t0 + th * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
             if (t < T && e < E) z[(size_t)t * E + e] = acc[i][j];
         }
     }
@@ -233,8 +280,8 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(
 int router_splits(int T, int D)
 {
     int want = (T <= 128) ? RT_MAX_SPLITS : (T <= 512) ? 4 : 1;
-    if (T >= RL_MIN_T)                          // one 32-token block per workgroup: aim for 256
-        while (want < 4 && (T + 31) / 32 * want < 256) want *= 2;
+    if (T >= RL_MIN_T)                          // one 64-token block per workgroup: aim for 256
+        while (want < RT_MAX_SPLITS && (T + RL_TOK - 1) / RL_TOK * want < 256) want *= 2;
     int s = want;
     while (s > 1 && (D / 64) % s != 0) --s;
     return s;
@@ -292,15 +339,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
 
     // logit = (split 0 + split 1 + ...) + bias; 0 marks an empty slot, every
     // real logit maps above 0 (NaN aside).  Every partial and bias of the
-    // token is loaded before any sum, so the loads cost one memory latency.
+    // token is loaded before any sum, so the loads cost one memory latency:
+    // the loads are unconditional (indices clamped to a real expert and
+    // split), and the empty asm statements take every loaded value before
+    // any is used, so the compiler cannot sink a load into a branch.
     float part[SLOTS][RT_MAX_SPLITS], bs[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
-        const bool in = lane + 64 * s < E;
-        bs[s] = in ? bias[lane + 64 * s] : 0.f;
+        const int ec = min(lane + 64 * s, E - 1);
+        bs[s] = bias[ec];
 #pragma unroll
         for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
-            part[s][sp] = (in && sp < splits) ? zp[((size_t)sp * T + t) * E + lane + 64 * s] : 0.f;
+            part[s][sp] = zp[((size_t)min(sp, splits - 1) * T + t) * E + ec];
+    }
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+        asm volatile("" : "+v"(bs[s]));
+#pragma unroll
+        for (int sp = 0; sp < RT_MAX_SPLITS; ++sp) asm volatile("" : "+v"(part[s][sp]));
     }
     uint32_t key[SLOTS];
 #pragma unroll
@@ -406,66 +462,71 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restric
                                                  __popcll(masks[2 * E + e]) + __popcll(masks[3 * E + e]);
 }
 
-// One workgroup: count[e] = sum over tiles; offset = exclusive scan of count;
-// tile_base[tile][e] = offset[e] + rows of expert e in earlier tiles.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t *__restrict__ tile_count,
-                                                         int ntiles, int E, int32_t *__restrict__ tile_base,
-                                                         int32_t *__restrict__ count,
-                                                         int32_t *__restrict__ offset)
-{
-    __shared__ int32_t sc[TOPK_MAX_E];
-    __shared__ int32_t ws[16];
-    const int tid = threadIdx.x;
-    // the per-tile counts are read eight tiles at a time (independent loads)
-    int c = 0;
-    if (tid < E) {
-        for (int tl0 = 0; tl0 < ntiles; tl0 += 8) {
-            int v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = (tl0 + k < ntiles) ? tile_count[(size_t)(tl0 + k) * E + tid] : 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) c += v[k];
-        }
-        count[tid] = c;
-    }
-    sc[tid] = block_scan_incl_1024((tid < E) ? c : 0, ws);
-    __syncthreads();
-    if (tid < E) {
-        int base = sc[tid] - c;           // exclusive prefix
-        offset[tid] = base;
-        if (tid == E - 1) offset[E] = sc[tid];
-        for (int tl0 = 0; tl0 < ntiles; tl0 += 8) {
-            int v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = (tl0 + k < ntiles) ? tile_count[(size_t)(tl0 + k) * E + tid] : 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (tl0 + k < ntiles) {
-                    tile_base[(size_t)(tl0 + k) * E + tid] = base;
-                    base += v[k];
-                }
-        }
-    }
-}
-
+// Every workgroup first forms its tile's first row per expert from the
+// counts of all tiles: offset[e] (exclusive scan over experts of the totals)
+// plus the expert's rows in earlier tiles.  Thread i holds experts 4 i ..
+// 4 i + 3 (E <= 1024); workgroup 0 also writes count and offset.  Then the
+// tile's masks are rebuilt and every assignment is written to its row.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
-                                                           int K, const int32_t *__restrict__ tile_base,
+                                                           int K, const int32_t *__restrict__ tile_count,
+                                                           int ntiles, int32_t *__restrict__ count,
+                                                           int32_t *__restrict__ offset,
                                                            int32_t *__restrict__ perm,
                                                            int32_t *__restrict__ inv)
 {
     __shared__ uint64_t masks[4 * TOPK_MAX_E];
-    build_tile_masks(ids, T, E, K, masks);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * PERM_TILE + threadIdx.x;
+    __shared__ int32_t first_s[TOPK_MAX_E];
+    __shared__ int32_t ws[4];
+    const int tid = threadIdx.x;
+    int tot[4] = {0, 0, 0, 0}, before[4] = {0, 0, 0, 0};
+    // eight tiles' counts at a time, unconditional loads of clamped indices
+    for (int tl0 = 0; tl0 < ntiles; tl0 += 8) {
+        int v[8][4];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[k][i] = tile_count[(size_t)min(tl0 + k, ntiles - 1) * E + min(4 * tid + i, E - 1)];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tl = tl0 + k;
+                tot[i] += (tl < ntiles) ? v[k][i] : 0;
+                before[i] += (tl < (int)blockIdx.x) ? v[k][i] : 0;
+            }
+    }
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (4 * tid + i >= E) tot[i] = 0;
+        local += tot[i];
+    }
+    const int incl = block_scan_incl<4>(local, ws);
+    int run = incl - local;                       // rows of the experts before 4 tid
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tid + i;
+        if (e < E) {
+            first_s[e] = run + before[i];
+            if (blockIdx.x == 0) {
+                count[e] = tot[i];
+                offset[e] = run;
+            }
+        }
+        run += tot[i];
+    }
+    if (blockIdx.x == 0 && tid == 255) offset[E] = incl;
+    build_tile_masks(ids, T, E, K, masks);        // its barriers also publish first_s
+    const int wave = tid >> 6, lane = tid & 63;
+    const int t = blockIdx.x * PERM_TILE + tid;
     if (t >= T) return;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int j = 0; j < K; ++j) {
         const int e = ids[(size_t)t * K + j];
         int rank = __popcll(masks[wave * E + e] & below);
         for (int w2 = 0; w2 < wave; ++w2) rank += __popcll(masks[w2 * E + e]);
-        const int row = tile_base[(size_t)blockIdx.x * E + e] + rank;
+        const int row = first_s[e] + rank;
         perm[row] = t * K + j;
         inv[(size_t)t * K + j] = row;
     }
@@ -551,13 +612,14 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
         const int n_mt = (T + RT_M - 1) / RT_M;
         if (T >= RL_MIN_T && E <= RL_MAX_E) {
             const int nfw = ((E + 31) / 32 + 3) / 4;
-            const unsigned g = splits * ((T + 31) / 32);
-            const int ns = router_lds_stages(E);
+            const unsigned g = splits * ((T + RL_TOK - 1) / RL_TOK);
+            int xs = 0, ws = 0;
+            router_lds_rings(E, &xs, &ws);
             const uint16_t *x = (const uint16_t *)a.x, *wr = (const uint16_t *)a.wr;
-            if (nfw == 1) router_logits_lds_kernel<1><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
-            else if (nfw == 2) router_logits_lds_kernel<2><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
-            else if (nfw == 3) router_logits_lds_kernel<3><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
-            else router_logits_lds_kernel<4><<<g, 256, 0, st>>>(x, wr, T, D, E, splits, ns, a.z);
+            if (nfw == 1) router_logits_lds_kernel<1><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
+            else if (nfw == 2) router_logits_lds_kernel<2><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
+            else if (nfw == 3) router_logits_lds_kernel<3><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
+            else router_logits_lds_kernel<4><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
         } else if (T <= 512)
             router_logits_bf16_kernel<1><<<splits * n_mt * ((E + 31) / 32), 256, 0, st>>>(
                 (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z);
@@ -588,8 +650,8 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
     }
     const int ntiles = perm_tiles(T);
     perm_hist_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_count);
-    perm_scan_kernel<<<1, 1024, 0, st>>>(a.tile_count, ntiles, E, a.tile_base, a.count, a.offset);
-    perm_scatter_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_base, a.perm, a.inv);
+    perm_scatter_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_count, ntiles, a.count, a.offset,
+                                                      a.perm, a.inv);
     mk.mark(st);
     return hipGetLastError();
 }

@@ -128,6 +128,10 @@ def test_int4_workload_sampled():
     (113, 33, 128, 50, 1, 64, "bf16"),       # K = 1
     (114, 70, 64, 1024, 8, 64, "bf16"),      # the largest supported E
     (115, 5, 64, 8, 8, 64, "f32"),
+    # several 256-token permutation tiles with a ragged last one: E = 1000 fills
+    # almost every thread's four experts, K = 6 leaves rows per tile uneven
+    (116, 1500, 64, 1000, 8, 64, "bf16"),
+    (117, 2100, 64, 288, 6, 64, "bf16"),
 ])
 def test_edge_shapes(cid, T, D, E, K, F, dt):
     cfg = custom_cfg(cid, T, D, E, K, F, dt)
