@@ -326,7 +326,7 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o)
 
 constexpr int TOPK_MAX_E = 1024;
 
-template <int SLOTS>
+template <int SLOTS, int NSP>          // NSP >= the number of reduction splits
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp, int splits,
                                                    const float *__restrict__ bias, int T, int E, int K,
                                                    int32_t *__restrict__ ids, float *__restrict__ w)
@@ -340,30 +340,33 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
     // logit = (split 0 + split 1 + ...) + bias; 0 marks an empty slot, every
     // real logit maps above 0 (NaN aside).  Every partial and bias of the
     // token is loaded before any sum, so the loads cost one memory latency:
-    // the loads are unconditional (indices clamped to a real expert and
-    // split), and the empty asm statements take every loaded value before
-    // any is used, so the compiler cannot sink a load into a branch.
-    float part[SLOTS][RT_MAX_SPLITS], bs[SLOTS];
+    // the loads are unconditional (the last slot's index clamped to a real
+    // expert, splits past the last clamped to it), and the empty asm
+    // statements take every loaded value before any is used, so the compiler
+    // cannot sink a load into a branch.  Slot s of lane l is expert 64 s + l,
+    // at a constant offset from the lane's first, so one address serves a row.
+    float part[SLOTS][NSP], bs[SLOTS];
+    auto col = [&](int s) { return (s < SLOTS - 1) ? lane + 64 * s : min(lane + 64 * s, E - 1); };
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-        const int ec = min(lane + 64 * s, E - 1);
-        bs[s] = bias[ec];
+    for (int s = 0; s < SLOTS; ++s) bs[s] = bias[col(s)];
 #pragma unroll
-        for (int sp = 0; sp < RT_MAX_SPLITS; ++sp)
-            part[s][sp] = zp[((size_t)min(sp, splits - 1) * T + t) * E + ec];
+    for (int sp = 0; sp < NSP; ++sp) {
+        const float *zr = zp + ((size_t)min(sp, splits - 1) * T + t) * E;
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) part[s][sp] = zr[col(s)];
     }
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
         asm volatile("" : "+v"(bs[s]));
 #pragma unroll
-        for (int sp = 0; sp < RT_MAX_SPLITS; ++sp) asm volatile("" : "+v"(part[s][sp]));
+        for (int sp = 0; sp < NSP; ++sp) asm volatile("" : "+v"(part[s][sp]));
     }
     uint32_t key[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
         float v = part[s][0];
 #pragma unroll
-        for (int sp = 1; sp < RT_MAX_SPLITS; ++sp)
+        for (int sp = 1; sp < NSP; ++sp)
             if (sp < splits) v += part[s][sp];
         key[s] = (lane + 64 * s < E) ? ordered_bits(v + bs[s]) : 0u;
     }
@@ -410,20 +413,22 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // weights p_j / sum p over the chosen experts in ascending id order.  When
-    // every chosen logit is negative the ratios are formed relative to the
-    // largest one so that tiny sigmoids cannot underflow the sum:
-    // sigmoid(a)/sigmoid(m) = e^(a-m) (1+e^m) / (1+e^a).
-    float zmax = sel_z_s[wave][0];
-    for (int j = 1; j < K; ++j) zmax = fmaxf(zmax, sel_z_s[wave][j]);
-    float psum = 0.f, pl = 0.f;
-    for (int j = 0; j < K; ++j) {
-        const float z = sel_z_s[wave][j];
-        const float pj = (zmax >= 0.f) ? sigmoid_f32(z)
-                                        : expf(z - zmax) * (1.0f + expf(zmax)) / (1.0f + expf(z));
-        psum += pj;
-        if (j == lane) pl = pj;
-    }
+    // weights p_j / sum p over the chosen experts, lane j holding chosen
+    // expert j (ascending id order).  When every chosen logit is negative the
+    // ratios are formed relative to the largest one so that tiny sigmoids
+    // cannot underflow the sum: sigmoid(a)/sigmoid(m) = e^(a-m) (1+e^m) / (1+e^a).
+    // The maximum and the sum over lanes 0..7 are butterflies (every lane
+    // ends with the same value, summed in the same order).
+    const float zl = (lane < K) ? sel_z_s[wave][lane] : -INFINITY;
+    float zmax = zl;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, o));
+    float pl = 0.f;
+    if (lane < K)
+        pl = (zmax >= 0.f) ? sigmoid_f32(zl) : expf(zl - zmax) * (1.0f + expf(zmax)) / (1.0f + expf(zl));
+    float psum = pl;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) psum += __shfl_xor(psum, o);
     if (lane < K) {
         ids[(size_t)t * K + lane] = sel_e_s[wave][lane];
         w[(size_t)t * K + lane] = pl / psum;
@@ -594,6 +599,16 @@ __global__ void route_empty_kernel(int E, int32_t *__restrict__ count, int32_t *
     }
 }
 
+template <int SLOTS>
+static void launch_topk(unsigned g, hipStream_t st, const float *z, int splits, const float *bias, int T, int E,
+                        int K, int32_t *ids, float *w)
+{
+    if (splits <= 1) topk_kernel<SLOTS, 1><<<g, 256, 0, st>>>(z, splits, bias, T, E, K, ids, w);
+    else if (splits <= 2) topk_kernel<SLOTS, 2><<<g, 256, 0, st>>>(z, splits, bias, T, E, K, ids, w);
+    else if (splits <= 4) topk_kernel<SLOTS, 4><<<g, 256, 0, st>>>(z, splits, bias, T, E, K, ids, w);
+    else topk_kernel<SLOTS, RT_MAX_SPLITS><<<g, 256, 0, st>>>(z, splits, bias, T, E, K, ids, w);
+}
+
 hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
 {
     const int T = a.T, D = a.D, E = a.E, K = a.K;
@@ -634,13 +649,13 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
     mk.mark(st);
     {
         const int g = (T + 3) / 4, slots = (E + 63) / 64;
-        if (slots <= 1) topk_kernel<1><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
-        else if (slots <= 2) topk_kernel<2><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
-        else if (slots <= 3) topk_kernel<3><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
-        else if (slots <= 4) topk_kernel<4><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
-        else if (slots <= 5) topk_kernel<5><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
-        else if (slots <= 8) topk_kernel<8><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
-        else topk_kernel<16><<<g, 256, 0, st>>>(a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        if (slots <= 1) launch_topk<1>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 2) launch_topk<2>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 3) launch_topk<3>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 4) launch_topk<4>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 5) launch_topk<5>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else if (slots <= 8) launch_topk<8>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
+        else launch_topk<16>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
     }
     mk.mark(st);
     if (T <= PERM_SMALL_T && E <= PERM_SMALL_MAX_E) {
