@@ -314,6 +314,15 @@ __device__ __forceinline__ const uint16_t *gateup_b_row(const uint16_t *G, const
     const int f = min(f0 + (blk >> 1) * 32 + (b & 31), F - 1);
     return ((blk & 1) ? U : G) + (size_t)f * D;
 }
+// The same in blocks of 16, for tiles whose waves hold one fragment each:
+// rows f0 + (b >> 5) * 16 .. +15 of gate, then the same rows of up, so a
+// fragment holds gate of 16 columns in lanes 0..15 and their up 16 lanes above.
+__device__ __forceinline__ const uint16_t *gateup_b_row16(const uint16_t *G, const uint16_t *U, int f0,
+                                                          int b, int D, int F)
+{
+    const int f = min(f0 + (b >> 5) * 16 + (b & 15), F - 1);
+    return (((b >> 4) & 1) ? U : G) + (size_t)f * D;
+}
 
 // Epilogue of the grouped kernels: accumulator element (m, n, i) of a lane is
 // tile row r0 + 32 m + 8 (i / 4) + i % 4 (r0 = the lane's first row: its
@@ -352,10 +361,10 @@ __global__ __launch_bounds__(256) void gateup_kernel(
     const int32_t *__restrict__ count, const int32_t *__restrict__ perm, int T, int D, int E, int K, int F,
     uint16_t *__restrict__ h)
 {
-    static_assert(C::FN % 2 == 0, "gate/up fragment pairs");
+    static_assert(C::FN % 2 == 0 || C::FN == 1, "gate/up fragment pairs, or gate/up halves of one fragment");
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
     constexpr int FC = C::BN / 2;                 // output columns per tile
-    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (F + FC - 1) / FC);
     if (et.e < 0) return;
     const int nt = et.ct;
     const uint16_t *G = et.shared ? s_gate : gate + (size_t)et.e * F * D;
@@ -378,12 +387,28 @@ __global__ __launch_bounds__(256) void gateup_kernel(
         ap[i] = x + (size_t)tok * D + ch0 * 8;
     }
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) bp[i] = gateup_b_row(G, U, f0, a_chunk_row<C>(i), D, F) + ch0 * 8;
+    for (int i = 0; i < C::B_PER_T; ++i)
+        bp[i] = (C::FN == 1 ? gateup_b_row16(G, U, f0, a_chunk_row<C>(i), D, F)
+                            : gateup_b_row(G, U, f0, a_chunk_row<C>(i), D, F)) + ch0 * 8;
     f32x16 acc[C::FM][C::FN];
     mfma_mainloop<C>(ap, bp, D, lds, acc);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
+    if constexpr (C::FN == 1) {
+        // lanes 0..15 (32..47) hold gate of h columns fl, the lanes 16 above their up
+        float upv[C::FM][16];
+#pragma unroll
+        for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) upv[m][i] = __shfl_xor(acc[m][0][i], 16);
+        const int fl = f0 + wn * 16 + (lane & 15);
+        frag_store_rows<C::FM, 1>(et, h + fl, (size_t)F, et.base, wm * C::FM * 32 + 4 * (lane >> 5),
+                                  (lane & 16) ? 0 : F - fl, [&](int m, int, int i) {
+                                      return f32_to_bf16_bits(swiglu_clamped_fast(acc[m][0][i], upv[m][i]));
+                                  });
+        return;
+    }
     // fragment pair (2p, 2p + 1) = gate and up of h columns fl + 32 p
     const int fl = f0 + wn * (C::FN / 2) * 32 + (lane & 31);
     frag_store_rows<C::FM, C::FN / 2>(et, h + fl, (size_t)F, et.base, wm * C::FM * 32 + 4 * (lane >> 5), F - fl,
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(256) void down_kernel(
     uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (D + TILE_N - 1) / TILE_N);
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (D + C::BN - 1) / C::BN);
     if (et.e < 0) return;
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
     const int d0 = et.ct * C::BN;                    // the last column tile may be ragged
@@ -925,6 +950,8 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 // launchers
 // ---------------------------------------------------------------------------
 using SmallCfg = TileCfg<32, 256, 1, 4>;
+using SmallGuCfg = TileCfg<32, 128, 1, 4>;
+using SmallDownCfg = TileCfg<32, 128, 1, 4>;
 constexpr int BIG_BM = BigCfg::BM;
 static_assert(SmallCfg::BN == TILE_N && I4Cfg<64>::BN == TILE_N && BigCfg::BN == TILE_N,
               "all paths cut columns alike");
@@ -955,19 +982,19 @@ static void launch_combine(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     mk.mark(st);
 }
 
-template <class C>
+template <class C, class CD>
 static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
     const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
-    const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
-    const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
+    const long grid_gu = xcd_grid(mt * ((a.F + C::BN / 2 - 1) / (C::BN / 2)));
+    const long grid_dn = xcd_grid(mt * ((a.D + CD::BN - 1) / CD::BN));
     mk.mark(st);
     gateup_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
         (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.perm,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);
-    down_kernel<C><<<(unsigned)grid_dn, 256, 0, st>>>(
+    down_kernel<CD><<<(unsigned)grid_dn, 256, 0, st>>>(
         (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
@@ -1025,7 +1052,7 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
             else
                 launch_staged_int4<I4Cfg<64>>(a, mk, st);
         } else if (a.bm == SmallCfg::BM) {
-            launch_staged<SmallCfg>(a, mk, st);
+            launch_staged<SmallGuCfg, SmallDownCfg>(a, mk, st);
         } else {
             launch_big(a, mk, st);
         }
