@@ -43,7 +43,7 @@ namespace coli {
 // barrier.  All waves reach the same answer.
 // ---------------------------------------------------------------------------
 constexpr int ROW_BLOCK = 8;
-constexpr int TILE_N = 256;          // columns of a tile in every bf16/int4 grouped kernel
+constexpr int TILE_N = 256;          // columns of a tile in the 256 x 256 and int4 grouped kernels
 
 // q / d for 0 <= q, d < 2^22 without an integer division (whose expansion
 // is several times longer): the float quotient from the hardware
@@ -949,18 +949,21 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-using SmallCfg = TileCfg<32, 256, 1, 4>;
+// row-light tiles: 32 rows x 128 columns (64 h columns per gate+up tile),
+// four workgroups per CU
 using SmallGuCfg = TileCfg<32, 128, 1, 4>;
 using SmallDownCfg = TileCfg<32, 128, 1, 4>;
+constexpr int SMALL_BM = SmallGuCfg::BM;
 constexpr int BIG_BM = BigCfg::BM;
-static_assert(SmallCfg::BN == TILE_N && I4Cfg<64>::BN == TILE_N && BigCfg::BN == TILE_N,
-              "all paths cut columns alike");
+static_assert(SmallDownCfg::BM == SMALL_BM && I4Cfg<32>::BM == SMALL_BM, "row-light paths share the tile height");
+static_assert(I4Cfg<64>::BN == TILE_N && I4Cfg<32>::BN == TILE_N && BigCfg::BN == TILE_N,
+              "the list-driven and int4 paths cut columns alike");
 
 int ffn_tile_rows(int T, int E, int K, int int4)
 {
     // rows per expert on average decides the tile height
     const long R = (long)T * K;
-    if (R <= 24L * E) return SmallCfg::BM;
+    if (R <= 24L * E) return SMALL_BM;
     return int4 ? I4Cfg<64>::BM : BIG_BM;
 }
 
@@ -1047,11 +1050,11 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
     StageMarks &mk = a.marks ? *a.marks : none;
     if (a.bf16) {
         if (a.use_int4) {
-            if (a.bm == SmallCfg::BM)
+            if (a.bm == SMALL_BM)
                 launch_staged_int4<I4Cfg<32>>(a, mk, st);
             else
                 launch_staged_int4<I4Cfg<64>>(a, mk, st);
-        } else if (a.bm == SmallCfg::BM) {
+        } else if (a.bm == SMALL_BM) {
             launch_staged<SmallGuCfg, SmallDownCfg>(a, mk, st);
         } else {
             launch_big(a, mk, st);

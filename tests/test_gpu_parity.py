@@ -39,6 +39,8 @@ SMALL = [
     # four reduction splits of four 64-wide steps each, ragged token blocks and expert fragments
     (106, 700, 1024, 500, 8, 64, "bf16", "uniform"),
     (107, 1000, 1024, 300, 8, 64, "bf16", "zipf"),
+    # row-light tiles (32 x 128) with a ragged last down tile (D = 192) and three h-column tiles
+    (108, 150, 192, 288, 8, 192, "bf16", "uniform"),
 ]
 
 
