@@ -840,14 +840,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= (long)T * per_row) return;
     const int t = (int)(q / per_row), d = (int)(q % per_row) * 8;
+    // all K row indices and weights, then all K rows, each round of loads in
+    // flight together: unconditional loads (slots past K reread slot K - 1;
+    // they are not summed), and the empty asm statements take every loaded
+    // value before any use, so the compiler cannot sink a load into a branch
     float wj[8];
+    int iv[8];
     u32x4 ov[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < K) {
-            wj[j] = w[(size_t)t * K + j];
-            ov[j] = *reinterpret_cast<const u32x4 *>(o + (size_t)inv[(size_t)t * K + j] * D + d);
-        }
+    for (int j = 0; j < 8; ++j) {
+        const size_t a = (size_t)t * K + min(j, K - 1);
+        wj[j] = w[a];
+        iv[j] = inv[a];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ov[j] = *reinterpret_cast<const u32x4 *>(o + (size_t)iv[j] * D + d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(ov[j]));
     const size_t idx = (size_t)t * D + d;
     const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sx + idx);
     const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sx + idx + 4);
