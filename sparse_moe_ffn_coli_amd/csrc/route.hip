@@ -444,6 +444,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
 // ---------------------------------------------------------------------------
 constexpr int PERM_TILE = 256;
 
+// The K (<= 8) expert ids of token t in one round of loads: unconditional
+// loads (slots past K reread slot K - 1), each value taken by an empty asm
+// statement before any use, so the compiler cannot sink a load into the
+// per-slot branch of its user (which costs one round trip per slot).
+__device__ __forceinline__ void load_token_ids(const int32_t *__restrict__ ids, int t, int K, int (&e)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = ids[(size_t)t * K + min(j, K - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(e[j]));
+}
+
 __device__ __forceinline__ void build_tile_masks(const int32_t *__restrict__ ids, int T, int E, int K,
                                                  uint64_t *masks)
 {
@@ -451,9 +463,13 @@ __device__ __forceinline__ void build_tile_masks(const int32_t *__restrict__ ids
     for (int i = threadIdx.x; i < 4 * E; i += PERM_TILE) masks[i] = 0ull;
     __syncthreads();
     const int t = blockIdx.x * PERM_TILE + threadIdx.x;
-    if (t < T)
-        for (int j = 0; j < K; ++j)
-            atomicOr((unsigned long long *)&masks[wave * E + ids[(size_t)t * K + j]], 1ull << lane);
+    if (t < T) {
+        int e[8];
+        load_token_ids(ids, t, K, e);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K) atomicOr((unsigned long long *)&masks[wave * E + e[j]], 1ull << lane);
+    }
     __syncthreads();
 }
 
@@ -527,8 +543,12 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
     const int t = blockIdx.x * PERM_TILE + tid;
     if (t >= T) return;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j = 0; j < K; ++j) {
-        const int e = ids[(size_t)t * K + j];
+    int ev[8];
+    load_token_ids(ids, t, K, ev);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j >= K) break;
+        const int e = ev[j];
         int rank = __popcll(masks[wave * E + e] & below);
         for (int w2 = 0; w2 < wave; ++w2) rank += __popcll(masks[w2 * E + e]);
         const int row = first_s[e] + rank;
@@ -558,9 +578,13 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
     __syncthreads();
-    if (tid < T)
-        for (int j = 0; j < K; ++j)
-            atomicOr((unsigned long long *)&masks[wave * E + ids[(size_t)tid * K + j]], 1ull << lane);
+    int ev[8];
+    if (tid < T) {
+        load_token_ids(ids, tid, K, ev);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K) atomicOr((unsigned long long *)&masks[wave * E + ev[j]], 1ull << lane);
+    }
     __syncthreads();
     int c = 0;
     if (tid < E)
@@ -574,8 +598,10 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
     }
     if (tid < T) {
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        for (int j = 0; j < K; ++j) {
-            const int e = ids[(size_t)tid * K + j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j >= K) break;
+            const int e = ev[j];
             int rank = __popcll(masks[wave * E + e] & below);
             for (int w2 = 0; w2 < wave; ++w2) rank += __popcll(masks[w2 * E + e]);
             const int row = (e > 0 ? sc[e - 1] : 0) + rank;   // exclusive prefix + rank
