@@ -213,10 +213,12 @@ __device__ __forceinline__ void xcd_split(int n, Cost &&cost, int32_t *__restric
     __syncthreads();
 }
 
-// One workgroup.  The counts are read from global memory once; the owner of
-// every row tile goes into an LDS table, so each list entry is computed once,
-// from LDS alone, together with its cost, which stays in LDS for the split.
-// Lists longer than the LDS tables recompute entries by binary search.
+// Two workgroups, one per list (both phases are bound by instruction issue on
+// one CU, so the lists are built side by side).  Each reads the counts once;
+// the owner of every row tile goes into an LDS table, so each list entry is
+// computed once, from LDS alone, together with its cost, which stays in LDS
+// for the split.  Lists longer than the LDS tables recompute entries by
+// binary search.
 constexpr int TILES_LDS_ROWS = 4096;     // row tiles with an owner entry in LDS
 constexpr int TILES_LDS_COST = 8192;     // entries per list with a cost in LDS
 
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
     __shared__ int32_t first_s[1024];
     __shared__ int32_t ws[16];
     __shared__ int16_t owner_s[TILES_LDS_ROWS];
-    __shared__ int16_t cost_gu[TILES_LDS_COST], cost_dn[TILES_LDS_COST];
+    __shared__ int16_t cost_s[TILES_LDS_COST];
     constexpr int BM = BigCfg::BM;
     const int tid = threadIdx.x;
     const int c = (tid < E) ? count[tid] : 0;
@@ -274,26 +276,20 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
                         : make_int4(e | (mn.y << 16), mn.x * BM, cnt[e], first_s[e]);
     };
     auto cost_of = [&](const int4 &en) { return TILE_COST0 + min(BM, en.z - en.y); };
-    const int n_gu = (routed + mt_sh) * nnt_gu, n_dn = (routed + mt_sh) * nnt_dn;
-    for (int q = tid; q < n_gu; q += 1024) {
-        const int4 en = entry(q, nnt_gu);
-        list_gu[q] = en;
-        if (q < TILES_LDS_COST) cost_gu[q] = (int16_t)cost_of(en);
+    // workgroup 0 builds the gate+up list, workgroup 1 the down list
+    const bool gu = blockIdx.x == 0;
+    const int nnt = gu ? nnt_gu : nnt_dn;
+    int4 *__restrict__ list = gu ? list_gu : list_dn;
+    const int n = (routed + mt_sh) * nnt;
+    for (int q = tid; q < n; q += 1024) {
+        const int4 en = entry(q, nnt);
+        list[q] = en;
+        if (q < TILES_LDS_COST) cost_s[q] = (int16_t)cost_of(en);
     }
-    for (int q = tid; q < n_dn; q += 1024) {
-        const int4 en = entry(q, nnt_dn);
-        list_dn[q] = en;
-        if (q < TILES_LDS_COST) cost_dn[q] = (int16_t)cost_of(en);
-    }
-    if (tid == 0) {
-        n_items[0] = n_dn;
-        n_items[1] = n_gu;
-    }
+    if (tid == 0) n_items[gu ? 1 : 0] = n;
     __syncthreads();
-    xcd_split(n_gu, [&](int q) { return q < TILES_LDS_COST ? (int)cost_gu[q] : cost_of(entry(q, nnt_gu)); },
-              n_items + 2);
-    xcd_split(n_dn, [&](int q) { return q < TILES_LDS_COST ? (int)cost_dn[q] : cost_of(entry(q, nnt_dn)); },
-              n_items + 2 + 9);
+    xcd_split(n, [&](int q) { return q < TILES_LDS_COST ? (int)cost_s[q] : cost_of(entry(q, nnt)); },
+              n_items + (gu ? 2 : 2 + 9));
 }
 
 // List entry of the 256 x 256 kernels: {e | ct << 16, m0, cnt, base}.
@@ -1018,7 +1014,7 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
     const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     mk.mark(st);
-    ffn_tiles_kernel<<<1, 1024, 0, st>>>(a.count, a.E, a.T, a.T * a.K, ffn_col_tiles_gu(a.F),
+    ffn_tiles_kernel<<<2, 1024, 0, st>>>(a.count, a.E, a.T, a.T * a.K, ffn_col_tiles_gu(a.F),
                                          ffn_col_tiles_dn(a.D), a.list_gu, a.list_dn, a.n_items);
     gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
