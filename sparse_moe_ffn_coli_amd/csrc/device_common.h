@@ -474,38 +474,51 @@ __device__ __forceinline__ void big_mainloop(const uint16_t *const (&rp)[C::CPW]
 }
 
 // ---------------------------------------------------------------------------
-// Streaming mode of the large-tile engine, for tiles with at most 32 real
+// Streaming mode of the large-tile engine, for tiles with at most 64 real
 // rows (experts with few tokens).  Such a tile is a stream of its 256 weight
 // rows with little arithmetic, so the LDS holds a deeper ring of small
-// stages: 32 A rows + 256 B rows of 128 bytes (36 KB) per step, NS = 4
-// stages, three in flight.  Each wave issues 5 copies per stage: one with
-// its first 32 lanes for A rows 4 w .. 4 w + 3 (512 bytes), four for B rows
-// as in big_mainloop.  Only the waves of the first row (wm = 0) multiply,
-// one 32-row fragment each.
+// stages: 64 A rows + 256 B rows of 128 bytes (40 KB) per step, NS = 4
+// stages, three in flight.  Each wave issues up to 5 copies per stage: one
+// for A rows 8 w .. 8 w + 7 (skipped when they all lie past the tile's real
+// rows), four for B rows as in big_mainloop.  The waves of the first two
+// rows (w < 4) multiply, one 32-row fragment each (A rows 32 (w / 2) ..,
+// skipped when that fragment has no real row), against B fragments
+// 4 (w % 2) .. + 3.
 // ---------------------------------------------------------------------------
 struct StreamCfg {
-    static constexpr int BK = 64, NS = 4;
-    static constexpr int A_BYTES = 32 * BK * 2;
+    static constexpr int BK = 64, NS = 4, A_ROWS = 64;
+    static constexpr int A_BYTES = A_ROWS * BK * 2;
     static constexpr int B_BYTES = 256 * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = NS * STAGE_BYTES;
-    static constexpr int CPW = 5;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-// Tile row of this lane's A copy (lanes 0..31 of wave w).
-__device__ __forceinline__ int stream_a_row(int w) { return w * 4 + ((threadIdx.x & 63) >> 3); }
+// Tile row of this lane's A copy (wave w).
+__device__ __forceinline__ int stream_a_row(int w) { return w * 8 + ((threadIdx.x & 63) >> 3); }
+
+// Wait until at most `pending` stages (0..2) of this wave's copies, cw per
+// stage (4 or 5), are in flight.
+__device__ __forceinline__ void stream_wait(int pending, int cw)
+{
+    if (pending == 0) wait_vmcnt_c<0>();
+    else if (cw == 4) { if (pending == 1) wait_vmcnt_c<4>(); else wait_vmcnt_c<8>(); }
+    else { if (pending == 1) wait_vmcnt_c<5>(); else wait_vmcnt_c<10>(); }
+}
 
 // ra: this lane's A source at k = 0 (row stream_a_row(w), chunk
-// big_copy_chunk<BigCfgT<64, 2>>(row) applied; lanes 32..63 unused); rb[j]:
-// B sources as the last four entries of big_mainloop's rp.
-__device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16_t *const (&rb)[4], int K, int w,
-                                                char *lds, f32x16 (&acc)[4])
+// big_copy_chunk<BigCfgT<64, 2>>(row) applied); rb[j]: B sources as the last
+// four entries of big_mainloop's rp; valid: real A rows of the tile (1..64).
+// acc: this wave's fragment products (waves 0..3).
+__device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16_t *const (&rb)[4], int K, int valid,
+                                                int w, char *lds, f32x16 (&acc)[4])
 {
     using C = StreamCfg;
     const int lane = threadIdx.x & 63;
     const int wn = w & 1;
-    const bool mma = (w >> 1) == 0;               // waves of the first row multiply
+    const bool mma = w < 4 && 32 * (w >> 1) < valid;   // a first-two-row wave with real rows
+    const bool acopy = 8 * w < valid;                   // this wave's A rows are not all padding
+    const int cw = acopy ? 5 : 4;
     const int nk = K / C::BK;
 
 #pragma unroll
@@ -516,10 +529,10 @@ __device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16
 #define COLI_ST_ISSUE(kt_)                                                                     \
     do {                                                                                       \
         char *st_ = lds + ((kt_) % C::NS) * C::STAGE_BYTES;                                    \
-        if (lane < 32)                                                                         \
+        if (acopy)                                                                             \
             __builtin_amdgcn_global_load_lds(                                                  \
                 (const __attribute__((address_space(1))) void *)(ra + (kt_) * C::BK),         \
-                (__attribute__((address_space(3))) void *)(st_ + w * 512), 16, 0, 0);         \
+                (__attribute__((address_space(3))) void *)(st_ + w * 1024), 16, 0, 0);        \
         _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                       \
             __builtin_amdgcn_global_load_lds(                                                  \
                 (const __attribute__((address_space(1))) void *)(rb[j_] + (kt_) * C::BK),     \
@@ -530,11 +543,9 @@ __device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
         if (s < nk) COLI_ST_ISSUE(s);
+    const int ra_ = 32 * (w >> 1) + (lane & 31);
     for (int kt = 0; kt < nk; ++kt) {
-        const int pending = min(C::NS - 2, nk - 1 - kt);      // stages after kt still in flight
-        if (pending >= 2) wait_vmcnt_c<2 * C::CPW>();
-        else if (pending == 1) wait_vmcnt_c<C::CPW>();
-        else wait_vmcnt_c<0>();
+        stream_wait(min(C::NS - 2, nk - 1 - kt), cw);     // stages after kt still in flight
         asm volatile("s_barrier" ::: "memory");               // see big_mainloop
         if (kt + C::NS - 1 < nk) COLI_ST_ISSUE(kt + C::NS - 1);
         if (mma) {
@@ -542,7 +553,6 @@ __device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16
 #pragma unroll
             for (int kk = 0; kk < C::BK / 16; ++kk) {
                 const int c = kk * 2 + (lane >> 5);
-                const int ra_ = lane & 31;
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + swz(ra_, c) * 2);
                 bf16x8 b[4];
 #pragma unroll

@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256) void down_kernel(
 
 // ---------------------------------------------------------------------------
 // 1/2 on the large-tile engine (row-heavy batches): 256 x 256 tiles, eight
-// waves.  A tile with at most 32 real rows runs the engine's streaming mode;
+// waves.  A tile with at most 64 real rows runs the engine's streaming mode;
 // otherwise each wave runs the variant for its number of real 32-row
 // fragments.
 // ---------------------------------------------------------------------------
@@ -549,7 +549,7 @@ __device__ __forceinline__ void gateup_big_tile(
     const uint16_t *U = et.shared ? s_up : up + (size_t)et.e * F * D;
     const int f0 = et.ct * (BigCfg::BN / 2);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (et.cnt - et.m0 <= 32) {
+    if (et.cnt - et.m0 <= StreamCfg::A_ROWS) {
         using S = StreamRows;
         const int row = stream_a_row(w);
         const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
@@ -565,11 +565,11 @@ __device__ __forceinline__ void gateup_big_tile(
             rb[j] = gateup_b_row(G, U, f0, br, D, F) + big_copy_chunk<S>(br) * 8;
         }
         f32x16 acc[4];
-        stream_mainloop(ra, rb, D, w, lds, acc);
-        if ((w >> 1) != 0) return;
+        stream_mainloop(ra, rb, D, et.cnt - et.m0, w, lds, acc);
+        if ((w >> 2) != 0) return;
         // fragment pair (2p, 2p + 1) = gate and up of h columns fl + 32 p
         const int fl = f0 + (w & 1) * 64 + (threadIdx.x & 31);
-        frag_store_rows<1, 2>(et, h + fl, (size_t)F, et.base, 4 * ((threadIdx.x & 63) >> 5), F - fl,
+        frag_store_rows<1, 2>(et, h + fl, (size_t)F, et.base, 32 * (w >> 1) + 4 * ((threadIdx.x & 63) >> 5), F - fl,
                               [&](int, int p, int i) {
                                   return f32_to_bf16_bits(swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
                               });
@@ -614,7 +614,7 @@ __device__ __forceinline__ void down_big_tile(
     const int d0 = et.ct * BigCfg::BN;
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (et.cnt - et.m0 <= 32) {
+    if (et.cnt - et.m0 <= StreamCfg::A_ROWS) {
         using S = StreamRows;
         const int row = stream_a_row(w);
         const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
@@ -626,14 +626,14 @@ __device__ __forceinline__ void down_big_tile(
             rb[j] = W + (size_t)min(d0 + br, D - 1) * F + big_copy_chunk<S>(br) * 8;
         }
         f32x16 acc[4];
-        stream_mainloop(ra, rb, F, w, lds, acc);
-        if ((w >> 1) != 0) return;
+        stream_mainloop(ra, rb, F, et.cnt - et.m0, w, lds, acc);
+        if ((w >> 2) != 0) return;
         const int dl = d0 + (w & 1) * 128 + (threadIdx.x & 31);
         if (et.shared)
-            frag_store_rows<1, 4>(et, sx + dl, (size_t)D, 0, 4 * ((threadIdx.x & 63) >> 5), D - dl,
+            frag_store_rows<1, 4>(et, sx + dl, (size_t)D, 0, 32 * (w >> 1) + 4 * ((threadIdx.x & 63) >> 5), D - dl,
                                   [&](int, int n, int i) { return acc[n][i]; });
         else
-            frag_store_rows<1, 4>(et, o + dl, (size_t)D, et.base, 4 * ((threadIdx.x & 63) >> 5), D - dl,
+            frag_store_rows<1, 4>(et, o + dl, (size_t)D, et.base, 32 * (w >> 1) + 4 * ((threadIdx.x & 63) >> 5), D - dl,
                                   [&](int, int n, int i) { return f32_to_bf16_bits(acc[n][i]); });
         return;
     }
