@@ -37,6 +37,7 @@ WORKLOAD_NAMES = {
     "prefill": "prefill T=4096, D=2048, F=768, 288 experts top-8 + 1 shared, bf16, Zipf(1.1) router bias",
     "decode": "decode T=64, D=2048, F=768, 288 experts top-8 + 1 shared, bf16",
     "int4": "int4 experts T=512, D=2048, F=768, 288 experts top-8 + 1 shared, group 32",
+    "int4_decode": "int4 experts decode T=64, D=2048, F=768, 288 experts top-8 + 1 shared, group 32",
     "tiny": "tiny T=8, D=128, F=64, 288 experts top-8 + 1 shared, fp32",
     "stacked": "stacked decode: 42 MoE layers, T=256, D=2048, F=768, 288 experts top-8 + 1 shared, "
                "bf16, fp32 residual stream",

@@ -15,6 +15,7 @@ expert width 768 are the workload definition's, the pages do not give them):
   int4     T=512,  D=2048, F=768, int4 experts (group 32, fp16 scales
            U(0.005, 0.02), nibbles U{0..15}), router + shared expert bf16
   stacked  T=256,  D=2048, F=768, bf16, 42 layers with independent weights
+  int4_decode  T=64, D=2048, F=768, int4 experts as in int4 (decode batch)
 
 Value recipe: x ~ N(0,1); router, gate, up ~ N(0, 1/D); down ~ N(0, 1/F);
 shared expert likewise; seed 0.  Token rows can be redrawn ("attempts") so
@@ -52,6 +53,8 @@ CONFIGS = {
                  layers=1, int4=True, group=32),
     "stacked": dict(cid=5, T=256, D=2048, E=288, K=8, F=768, dtype="bf16", bias="uniform",
                     layers=42, int4=False),
+    "int4_decode": dict(cid=6, T=64, D=2048, E=288, K=8, F=768, dtype="bf16", bias="uniform",
+                        layers=1, int4=True, group=32),
 }
 ZIPF_S = 1.1
 GAP_MIN = 1e-3

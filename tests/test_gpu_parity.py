@@ -121,6 +121,36 @@ def test_int4_workload_sampled():
             compare(got, ref, cfg, tokens=toks, label="int4"))
 
 
+def test_int4_decode():
+    # decode batch (T = 64) with int4 experts: every output token against the oracle
+    cfg = synth.CONFIGS["int4_decode"]
+    W = synth.workload("int4_decode")
+    _report("int4 decode", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4 decode"))
+
+
+def test_int4_stacked_layer_shape_sampled():
+    # one layer of the stacked decode shape (T = 256) with int4 experts; tokens and
+    # router are the stacked workload's first layer, whose stored redraws keep the
+    # 8th and 9th router probabilities apart
+    import oracle
+    cfg = dict(synth.CONFIGS["stacked"], layers=1, int4=True, group=32)
+    W = synth.layer_weights(cfg, 0)
+    W["x"] = synth.x_rows(cfg, synth.load_attempts("stacked"))
+    got = run_gpu(W, cfg)
+    T, D, E, K, F, G = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], cfg["group"]
+    z = oracle.router_logits(W["x"], W["wr"], W["bias"], T, D, E)
+    ids, w = oracle.select_topk(z, K)
+    count, offset, perm, inv = oracle.permutation(ids, E)
+    toks = sample_tokens(ids, count, T)
+    Mi = oracle.Mat.int4
+    y = oracle.moe_ffn(W["x"], ids, w, Mi(W["gate_q"], W["gate_s"], G), Mi(W["up_q"], W["up_s"], G),
+                       Mi(W["down_q"], W["down_s"], G), W["s_gate"], W["s_up"], W["s_down"],
+                       T, D, E, K, F, tokens=toks)
+    ref = dict(ids=ids, w=w, count=count, offset=offset, perm=perm, inv=inv, y=y)
+    _report(f"int4 stacked-layer shape ({len(toks)} sampled tokens)",
+            compare(got, ref, cfg, tokens=toks, label="int4 T=256"))
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
