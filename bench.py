@@ -13,7 +13,7 @@ Prints ONE JSON line.  Besides the throughput it reports
                 events recorded around that kernel inside the timed region;
   cpu_baseline: the CPU oracle timed on a bounded sample of the same inputs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|int4|tiny]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|int4|int4_decode|stacked|tiny]
 """
 import argparse
 import csv

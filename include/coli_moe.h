@@ -163,8 +163,10 @@ coli_status coli_moe_ffn_int4(const coli_moe_shape *s, const void *x,
  * after the last one.  Entries past n_events, and NULL entries, are skipped.
  * Nothing is recorded when the call fails validation or T = 0.
  *   route stages (3): router logits, top-K, permutation
- *   ffn stages (3):   gate+up (+SwiGLU; for large batches also the kernel
- *                     that lists the tiles), down (routed and shared), combine */
+ *   ffn stages (3):   gate+up (+SwiGLU), down (routed and shared), combine;
+ *                     a preparation kernel (the tile lists for large batches,
+ *                     the x -> fp16 pass for int4) runs before events[0], so
+ *                     events[0..1] bracket the gate+up kernel alone */
 coli_status coli_moe_route_timed(const coli_moe_shape *s, const void *x, const void *w_router,
                                  const float *bias, const coli_moe_routing *out, void *ws,
                                  size_t ws_bytes, void *stream, void *const *events,

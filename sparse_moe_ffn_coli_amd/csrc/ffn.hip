@@ -1013,9 +1013,9 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     const long mt = ffn_max_tiles(a.T, a.E, a.K, BigCfg::BM);
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
     const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
-    mk.mark(st);
     ffn_tiles_kernel<<<2, 1024, 0, st>>>(a.count, a.E, a.T, a.T * a.K, ffn_col_tiles_gu(a.F),
                                          ffn_col_tiles_dn(a.D), a.list_gu, a.list_dn, a.n_items);
+    mk.mark(st);                                     // the gate+up stage is its kernel alone
     gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
         (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.perm, a.list_gu, a.n_items,
@@ -1034,8 +1034,8 @@ static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t s
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
     const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
     const long n8 = (long)a.T * a.D / 8;
-    mk.mark(st);
     x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint16_t *)a.x, n8, a.x16);
+    mk.mark(st);                                     // the gate+up stage is its kernel alone
     gateup_int4_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         a.x16, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
         (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.perm,
