@@ -41,6 +41,10 @@ SMALL = [
     (107, 1000, 1024, 300, 8, 64, "bf16", "zipf"),
     # row-light tiles (32 x 128) with a ragged last down tile (D = 192) and three h-column tiles
     (108, 150, 192, 288, 8, 192, "bf16", "uniform"),
+    # the 256 x 256 engine's streaming-mode boundary: experts average 64 rows, so tiles of
+    # just under and just over 64 rows; the shared expert's last tile has 64 rows, then 65
+    (109, 320, 128, 40, 8, 64, "bf16", "uniform"),
+    (110, 321, 128, 40, 8, 64, "bf16", "uniform"),
 ]
 
 
