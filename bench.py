@@ -14,6 +14,7 @@ Prints ONE JSON line.  Besides the throughput it reports
   cpu_baseline: the CPU oracle timed on a bounded sample of the same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|int4|int4_decode|stacked|tiny]
+                [--tokens T]
 """
 import argparse
 import csv
@@ -209,18 +210,30 @@ def roofline(flops, nbytes, seconds, peak_flops):
 # ---------------------------------------------------------------------------
 # one workload on the GPU
 # ---------------------------------------------------------------------------
-def run_workload(name, steps, warmup, hip):
+def workload_inputs(name, tokens=None):
+    """Config and inputs of workload ``name``; ``tokens`` overrides its batch
+    size (token rows then drawn without the stored 8th/9th-gap redraws, which
+    only the parity tests need)."""
+    import synth
+
+    if tokens is None:
+        return synth.CONFIGS[name], synth.workload(name)
+    cfg = dict(synth.CONFIGS[name], T=int(tokens))
+    W = synth.layer_weights(cfg, 0)
+    W["x"] = synth.x_rows(cfg, None, 0)
+    return cfg, W
+
+
+def run_workload(name, steps, warmup, hip, tokens=None):
     import numpy as np
     import torch
 
-    import synth
     from sparse_moe_ffn_coli_amd import COLI_BF16, COLI_F32, FFN_STAGES, ROUTE_STAGES
     from sparse_moe_ffn_coli_amd.layer import DeviceLayer, to_device
 
-    cfg = synth.CONFIGS[name]
-    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
     t0 = time.time()
-    W = synth.workload(name)
+    cfg, W = workload_inputs(name, tokens)
+    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
     log(f"{name}: generated inputs in {time.time() - t0:.1f}s")
     dt = COLI_F32 if cfg["dtype"] == "f32" else COLI_BF16
     layer = DeviceLayer(W, T, D, E, K, F, dt, group=cfg.get("group", 32))
@@ -367,17 +380,15 @@ def run_stacked(steps, warmup, hip):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
-def cpu_baseline(name, budget_s=15.0):
+def cpu_baseline(name, budget_s=15.0, tokens=None):
     import numpy as np
 
     import oracle
-    import synth
 
-    cfg = synth.CONFIGS[name]
-    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
     if name == "stacked":
         return cpu_baseline_stacked(budget_s)
-    W = synth.workload(name)
+    cfg, W = workload_inputs(name, tokens)
+    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
     if cfg.get("int4"):
         G = cfg["group"]
         g = oracle.Mat.int4(W["gate_q"], W["gate_s"], G)
@@ -435,6 +446,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's batch size T (not for stacked)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -459,22 +472,26 @@ def main():
     if args.copy_calibration:
         copy_calibration()
 
+    if args.tokens is not None and (args.workload == "stacked" or args.tokens < 1):
+        print("--tokens takes a positive batch size and a single-layer workload", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "stacked":
         main_res = run_stacked(args.steps, args.warmup, hip)
     else:
-        main_res = run_workload(args.workload, args.steps, args.warmup, hip)
+        main_res = run_workload(args.workload, args.steps, args.warmup, hip, args.tokens)
     dec = None
-    if args.workload == "prefill" and not args.no_decode:
+    if args.workload == "prefill" and not args.no_decode and args.tokens is None:
         dec = run_workload("decode", args.steps, args.warmup, hip)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(args.workload)
+        cpu = cpu_baseline(args.workload, tokens=args.tokens)
         log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} threads")
 
     cfg = main_res["cfg"]
     out = {
-        "metric": ("routed-MoE tokens/s at T=4096 prefill" if args.workload == "prefill" else
+        "metric": (f"routed-MoE tokens/s ({args.workload}, T={cfg['T']})" if args.tokens is not None else
+                   "routed-MoE tokens/s at T=4096 prefill" if args.workload == "prefill" else
                    "routed-MoE tokens/s, 42-layer stacked decode (T=256)" if args.workload == "stacked"
                    else f"routed-MoE tokens/s ({args.workload})"),
         "value": round(main_res["tokens_per_s"], 1),
@@ -488,11 +505,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if cfg["dtype"] == "f32" else ("fp16 (int4 weights)" if cfg.get("int4") else "bf16"),
         "data": "synthetic (seeded generator, seed 0)",
-        "config": {"workload": WORKLOAD_NAMES[args.workload], "global_batch": cfg["T"],
+        "config": {"workload": WORKLOAD_NAMES[args.workload] + (
+                       f", batch overridden to T={cfg['T']}" if args.tokens is not None else ""),
+                   "global_batch": cfg["T"],
                    "seq_len": 1, "parallelism": "none (one GPU)", "experts": cfg["E"],
                    "top_k": cfg["K"], "d_model": cfg["D"], "d_ff": cfg["F"],
                    "nonempty_experts": main_res["n_e"]},
-        "roofline": dict(main_res["roofline"], traffic=recorded_traffic(args.workload, "gateup"),
+        "roofline": dict(main_res["roofline"],
+                         traffic=None if args.tokens is not None else recorded_traffic(args.workload, "gateup"),
                          kernel="gate_up", avg_us=round(main_res["gu_s"] * 1e6, 2),
                          algorithmic_bytes=main_res["gate_up_work"]["bytes"],
                          algorithmic_flops=main_res["gate_up_work"]["flops"]),
