@@ -86,6 +86,10 @@ def lib():
         L.oracle_residual_layer.argtypes = [i64, i64, i64, i32, i64, vp, mp, vp,
                                             mp, mp, mp, mp, mp, mp,
                                             vp, vp, vp, vp, vp, vp]
+        L.oracle_dense_ffn.restype = i32
+        L.oracle_dense_ffn.argtypes = [i64, i64, i64, mp, mp, mp, mp, vp, vp]
+        L.oracle_index_topk.restype = i32
+        L.oracle_index_topk.argtypes = [i64, i64, i64, vp, vp, i64, i64, vp]
         L.oracle_num_threads.restype = i32
         L.oracle_num_threads.argtypes = []
         _lib = L
@@ -303,6 +307,32 @@ def residual_layer(x, wr, bias, gate, up, down, s_gate, s_up, s_down, D, E, K, F
                                        *[m.ref() for m in mats], _p(xin), _p(ids),
                                        _p(w), _p(z), _p(y), _p(xn)), "residual_layer")
     return xin, ids, w, z, y, xn
+
+
+def dense_ffn(x, gate, up, down, T, D, F, residual=None):
+    """Dense FFN layer: y = residual + W_down swiglu(W_gate x, W_up x) for all T rows."""
+    x = _as_mat(x)
+    mats = [_as_mat(a) for a in (gate, up, down)]
+    if residual is not None:
+        residual = np.ascontiguousarray(residual, dtype=np.float64)
+    y = np.empty((T, D), np.float64)
+    _check(lib().oracle_dense_ffn(T, D, F, x.ref(), *[m.ref() for m in mats],
+                                  None if residual is None else _p(residual), _p(y)),
+           "dense_ffn")
+    return y
+
+
+def index_topk(scores, k, tail=0, lens=None):
+    """Selected positions per row of ``scores`` (float32 [rows][L]), ascending, -1 padded."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    rows, L = scores.shape
+    if lens is not None:
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+    idx = np.empty((rows, k), np.int32)
+    _check(lib().oracle_index_topk(rows, L, L, _p(scores) if rows else None,
+                                   None if lens is None else _p(lens), k, tail,
+                                   _p(idx) if rows else None), "index_topk")
+    return idx
 
 
 def sigma_gap(z, K):

@@ -377,3 +377,93 @@ int oracle_residual_layer(int64_t n, int64_t D, int64_t E, int K, int64_t F,
     if (!z) free(zz);
     return rc;
 }
+
+/* ------------------------------------------------------------------ */
+/* dense FFN (layers without experts)                                  */
+/* ------------------------------------------------------------------ */
+
+int oracle_dense_ffn(int64_t T, int64_t D, int64_t F, const orc_mat *x,
+                     const orc_mat *gate, const orc_mat *up, const orc_mat *down,
+                     const double *residual, double *y)
+{
+    if (T < 0 || D <= 0 || F <= 0 || !y || !mat_ok(x, D) || !mat_ok(gate, D) ||
+        !mat_ok(up, D) || !mat_ok(down, F))
+        return ORC_E_ARG;
+    int bad = 0;
+    int64_t t;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (t = 0; t < T; ++t) {
+        double *xr = (double *)malloc((size_t)D * sizeof(double));
+        double *h = (double *)malloc((size_t)F * sizeof(double));
+        if (!xr || !h) { bad = 1; free(xr); free(h); continue; }
+        widen_row(x, 0, T, D, t, xr);
+        oracle_expert_hidden(D, F, xr, gate, up, 1, 0, h);
+        oracle_expert_down(D, F, h, down, 1, 0, y + t * D);
+        if (residual)
+            for (int64_t d = 0; d < D; ++d) y[t * D + d] = residual[t * D + d] + y[t * D + d];
+        free(xr);
+        free(h);
+    }
+    return bad ? ORC_E_ARG : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* index selection (top-k over indexer scores, tail always kept)       */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    int tail;      /* 1: one of the always-selected last positions */
+    double score;
+    int64_t pos;
+} orc_cand;
+
+/* a ranks before b: tail positions first, then larger score, then lower position */
+static int cand_cmp(const void *pa, const void *pb)
+{
+    const orc_cand *a = (const orc_cand *)pa, *b = (const orc_cand *)pb;
+    if (a->tail != b->tail) return a->tail ? -1 : 1;
+    if (a->score > b->score) return -1;
+    if (a->score < b->score) return 1;
+    return (a->pos < b->pos) ? -1 : (a->pos > b->pos);
+}
+
+static int pos_cmp(const void *pa, const void *pb)
+{
+    const int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+int oracle_index_topk(int64_t rows, int64_t L, int64_t ld, const float *scores,
+                      const int32_t *lens, int64_t k, int64_t tail, int32_t *idx)
+{
+    if (rows < 0 || L < 0 || ld < L || k <= 0 || tail < 0 || (rows > 0 && (!scores || !idx)))
+        return ORC_E_ARG;
+    int bad = 0;
+    int64_t r;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (r = 0; r < rows; ++r) {
+        int64_t n = L;
+        if (lens) {
+            if (lens[r] < 0) { bad = 1; continue; }
+            if (lens[r] < n) n = lens[r];
+        }
+        int32_t *out = idx + r * k;
+        if (n <= k) {
+            for (int64_t j = 0; j < k; ++j) out[j] = j < n ? (int32_t)j : -1;
+            continue;
+        }
+        orc_cand *c = (orc_cand *)malloc((size_t)n * sizeof(orc_cand));
+        if (!c) { bad = 1; continue; }
+        const int64_t nt = tail < k ? tail : k;
+        for (int64_t i = 0; i < n; ++i) {
+            c[i].tail = i >= n - nt;
+            c[i].score = (double)scores[r * ld + i];
+            c[i].pos = i;
+        }
+        qsort(c, (size_t)n, sizeof(orc_cand), cand_cmp);
+        for (int64_t j = 0; j < k; ++j) out[j] = (int32_t)c[j].pos;
+        qsort(out, (size_t)k, sizeof(int32_t), pos_cmp);
+        free(c);
+    }
+    return bad ? ORC_E_ARG : 0;
+}

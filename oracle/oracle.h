@@ -121,6 +121,32 @@ int oracle_residual_layer(int64_t n, int64_t D, int64_t E, int K, int64_t F,
                           uint16_t *xin_bf16, int32_t *ids, double *w, double *z,
                           double *y, double *x_next);
 
+/*
+ * Dense FFN layer ([glm5next] "Architecture" and "MoE FFN": the first three
+ * layers run a dense FFN with no experts; the clamped SwiGLU is stated for
+ * the model as a whole):
+ *   y[t] = residual[t] + W_down swiglu(W_gate x_t, W_up x_t)
+ * gate/up [F][D], down [D][F]; residual nullable [T][D]; y [T][D].
+ */
+int oracle_dense_ffn(int64_t T, int64_t D, int64_t F, const orc_mat *x,
+                     const orc_mat *gate, const orc_mat *up, const orc_mat *down,
+                     const double *residual, double *y);
+
+/*
+ * Index selection of the sparse attention's IndexPool ([glm5next] "MLA/DSA":
+ * top-k over the indexer scores with k = 2048, and the last kpool tokens
+ * always selected).  Per row r of scores [rows][ld] (fp32), over its first
+ * n = min(lens[r], L) positions (n = L when lens is NULL):
+ *   - n <= k: every position 0..n-1 is selected;
+ *   - otherwise the last min(tail, k) positions n - tail .. n - 1 are
+ *     selected, and the remaining slots go to the other positions in order of
+ *     score, larger first, ties to the lower position.
+ * idx[r][0..k-1] holds the selected positions in ascending order, then -1 in
+ * the slots left over when n < k.
+ */
+int oracle_index_topk(int64_t rows, int64_t L, int64_t ld, const float *scores,
+                      const int32_t *lens, int64_t k, int64_t tail, int32_t *idx);
+
 /* Threads the OpenMP loops use (1 when built without OpenMP). */
 int oracle_num_threads(void);
 

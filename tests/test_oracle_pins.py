@@ -468,3 +468,115 @@ def test_sigma_gap_helper():
     z = np.array([[5.0, 4.0, 3.0, 0.0, 0.0, 0.0, 0.0, 0.0, -1.0, -2.0]])
     # 8th largest = 0 (index 7), 9th = -1
     assert oracle.sigma_gap(z, 8)[0] == pytest.approx(0.5 - 0.2689414213699951, abs=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# dense FFN layers ([glm5next] "Architecture": layers 0-2 run a dense FFN with
+# no experts; the clamped SwiGLU holds for the model's FFNs)
+# ---------------------------------------------------------------------------
+
+def test_dense_ffn_hand_points():
+    # D = 2, F = 1: g = x0, u = x1, y = (1, 3) * silu(min(g, 10)) * clamp(u)
+    gate = np.array([[1.0, 0.0]], np.float32)
+    up = np.array([[0.0, 1.0]], np.float32)
+    down = np.array([[1.0], [3.0]], np.float32)
+    x = np.array([[1.0, 2.0], [20.0, 20.0], [-1.0, -30.0]], np.float32)
+    y = oracle.dense_ffn(x, gate, up, down, 3, 2, 1)
+    h = [2 * 0.7310585786300049,          # silu(1) * 2
+         99.99546021312977,               # silu(10) * 10: both clamps
+         -0.2689414213699951 * -10.0]     # silu(-1) * (-10): up clamped below
+    np.testing.assert_allclose(y, [[v, 3 * v] for v in h], rtol=1e-14)
+    res = np.array([[0.5, -0.5], [1.0, 2.0], [0.0, 0.0]])
+    y2 = oracle.dense_ffn(x, gate, up, down, 3, 2, 1, residual=res)
+    np.testing.assert_allclose(y2, y + res, rtol=1e-15)
+
+
+def test_dense_ffn_matches_textbook_swiglu_ffn():
+    # bf16 operands with D != F (a transposed down projection would not fit),
+    # inputs scaled so both clamps fire
+    rng = np.random.default_rng(7)
+    T, D, F = 6, 48, 80
+
+    def bf16(a):
+        b = np.array([oracle.bf16_from_double(float(v)) for v in a.reshape(-1)], np.uint16)
+        return b.reshape(a.shape)
+
+    def wide(b):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    x, g, u, d = (bf16(rng.standard_normal(s) * sc) for s, sc in
+                  (((T, D), 6.0), ((F, D), 0.5), ((F, D), 0.5), ((D, F), 0.2)))
+    y = oracle.dense_ffn(Mat.bf16(x), Mat.bf16(g), Mat.bf16(u), Mat.bf16(d), T, D, F)
+    gg = wide(x) @ wide(g).T
+    uu = wide(x) @ wide(u).T
+    assert (gg > 10).any() and (np.abs(uu) > 10).any()
+    gc = np.minimum(gg, 10.0)
+    hh = gc / (1.0 + np.exp(-gc)) * np.clip(uu, -10.0, 10.0)
+    np.testing.assert_allclose(y, hh @ wide(d).T, rtol=1e-10, atol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# index selection ([glm5next] "MLA/DSA": top-k of the indexer scores with
+# k = 2048; the last kpool positions always selected)
+# ---------------------------------------------------------------------------
+
+def test_index_topk_hand_example():
+    s = np.array([[3, 1, 3, 2, 5, 0, 1, 1, 2, 4]], np.float32)
+    # 5 at 4, 4 at 9, then 3 at 0 and 2 tie: the lower position wins
+    assert oracle.index_topk(s, 3).tolist() == [[0, 4, 9]]
+    # tail 2 keeps positions 8 and 9, the one free slot goes to the 5 at position 4
+    assert oracle.index_topk(s, 3, tail=2).tolist() == [[4, 8, 9]]
+    # the first 6 positions only: 5 at 4, 3 at 0 and 2
+    assert oracle.index_topk(s, 3, lens=[6]).tolist() == [[0, 2, 4]]
+    # k = 4 with the tail at positions 4, 5 of the first 6: then 3, 3 at 0 and 2
+    assert oracle.index_topk(s, 4, tail=2, lens=[6]).tolist() == [[0, 2, 4, 5]]
+
+
+def test_index_topk_short_rows_take_everything():
+    s = np.arange(12, dtype=np.float32).reshape(2, 6)[:, ::-1].copy()
+    out = oracle.index_topk(s, 8, lens=[6, 0])
+    assert out[0].tolist() == [0, 1, 2, 3, 4, 5, -1, -1]
+    assert out[1].tolist() == [-1] * 8
+    assert oracle.index_topk(s, 6).tolist() == [list(range(6))] * 2
+
+
+def test_index_topk_signed_zero_and_infinities_order():
+    s = np.array([[0.0, -0.0, -np.inf, 1e-45, -1e-45, np.inf, -0.0]], np.float32)
+    # inf; the smallest positive subnormal; then +0 and -0 tie: positions 0 and 1
+    assert oracle.index_topk(s, 4).tolist() == [[0, 1, 3, 5]]
+    assert oracle.index_topk(s, 6).tolist() == [[0, 1, 3, 4, 5, 6]]
+
+
+def test_index_topk_matches_lexsort_brute_force():
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        rows, L = 3, int(rng.integers(1, 60))
+        s = rng.integers(0, 5, size=(rows, L)).astype(np.float32)   # many ties
+        k = int(rng.integers(1, 40))
+        tail = int(rng.integers(0, 6))
+        lens = rng.integers(0, L + 3, size=rows).astype(np.int32)
+        got = oracle.index_topk(s, k, tail=tail, lens=lens)
+        for r in range(rows):
+            n = min(int(lens[r]), L)
+            pos = np.arange(n)
+            if n <= k:
+                want = list(range(n)) + [-1] * (k - n)
+            else:
+                is_tail = pos >= n - min(tail, k)
+                order = np.lexsort((pos, -s[r, :n], ~is_tail))
+                want = sorted(order[:k].tolist())
+            assert got[r].tolist() == want, (trial, r)
+
+
+def test_index_topk_invariants_at_scale():
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((4, 5000)).astype(np.float32)
+    k, tail = 2048, 4
+    out = oracle.index_topk(s, k, tail=tail)
+    for r in range(4):
+        sel = out[r]
+        assert len(set(sel.tolist())) == k and np.all(np.diff(sel) > 0)
+        assert set(range(5000 - tail, 5000)) <= set(sel.tolist())
+        rest = np.setdiff1d(np.arange(5000 - tail), sel)
+        chosen = np.setdiff1d(sel, np.arange(5000 - tail, 5000))
+        assert s[r, chosen].min() >= s[r, rest].max()
