@@ -12,6 +12,13 @@ The entry points keep the C names:
   coli_moe_route(shape, x, w_router, bias, routing, ws, stream=None)
   coli_moe_ffn(shape, x, routing, weights, y, residual=None, y_bf16=None, ws, stream=None)
   coli_moe_ffn_int4(shape, x, routing, weights_int4, y, residual=None, y_bf16=None, ws, stream=None)
+  coli_moe_dense_workspace_bytes(shape) -> int
+  coli_moe_dense_ffn(shape, x, dense_weights, y, residual=None, y_bf16=None, ws, stream=None)
+  coli_moe_bank_fill(shape, host_tensors, bank_tensors, experts=None, int4=False, group=32,
+                     copy_stream, wait_event=None, ready_event=None)
+  coli_moe_bank_acquire(compute_stream, ready_event) / coli_moe_bank_release(compute_stream, free_event)
+  coli_index_topk_workspace_bytes(rows, L, k) -> int
+  coli_index_topk(scores, k, idx, tail=0, lens=None, ws=None, stream=None)
   coli_moe_status_str(code) -> str
 
 If the library has not been built the import still works, but every call
@@ -30,9 +37,12 @@ LIB_PATH = os.path.join(_HERE, "libcoli_moe.so")
 COLI_F32, COLI_BF16 = 0, 1
 STATUS_NAMES = {0: "COLI_OK", 1: "COLI_E_NULL", 2: "COLI_E_SHAPE", 3: "COLI_E_DTYPE",
                 4: "COLI_E_ALIGN", 5: "COLI_E_WORKSPACE", 6: "COLI_E_DEVICE",
-                7: "COLI_E_LAUNCH", 8: "COLI_E_ALIAS"}
+                7: "COLI_E_LAUNCH", 8: "COLI_E_ALIAS", 9: "COLI_E_MEMORY"}
 EXPORTED = ("coli_moe_workspace_bytes", "coli_moe_route", "coli_moe_ffn", "coli_moe_ffn_int4",
             "coli_moe_route_timed", "coli_moe_ffn_timed", "coli_moe_ffn_int4_timed",
+            "coli_moe_dense_workspace_bytes", "coli_moe_dense_ffn",
+            "coli_moe_bank_fill", "coli_moe_bank_acquire", "coli_moe_bank_release",
+            "coli_index_topk_workspace_bytes", "coli_index_topk",
             "coli_moe_status_str", "coli_moe_version")
 ROUTE_STAGES = ("router", "topk", "perm")
 FFN_STAGES = ("gate_up", "down", "combine")
@@ -71,6 +81,10 @@ class CWeightsInt4(C.Structure):
                 ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p)]
 
 
+class CDenseWeights(C.Structure):
+    _fields_ = [("gate", C.c_void_p), ("up", C.c_void_p), ("down", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -101,6 +115,23 @@ def lib():
         L.coli_moe_ffn_timed.argtypes = L.coli_moe_ffn.argtypes + [ev, C.c_int32]
         L.coli_moe_ffn_int4_timed.restype = C.c_int
         L.coli_moe_ffn_int4_timed.argtypes = L.coli_moe_ffn_int4.argtypes + [ev, C.c_int32]
+        L.coli_moe_dense_workspace_bytes.restype = sz
+        L.coli_moe_dense_workspace_bytes.argtypes = [sp]
+        L.coli_moe_dense_ffn.restype = C.c_int
+        L.coli_moe_dense_ffn.argtypes = [sp, vp, C.POINTER(CDenseWeights), vp, vp, vp, vp, sz, vp]
+        L.coli_moe_bank_fill.restype = C.c_int
+        L.coli_moe_bank_fill.argtypes = [sp, C.c_int32, C.c_int32, C.POINTER(C.c_void_p),
+                                         C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.c_int32,
+                                         vp, vp, vp]
+        L.coli_moe_bank_acquire.restype = C.c_int
+        L.coli_moe_bank_acquire.argtypes = [vp, vp]
+        L.coli_moe_bank_release.restype = C.c_int
+        L.coli_moe_bank_release.argtypes = [vp, vp]
+        L.coli_index_topk_workspace_bytes.restype = sz
+        L.coli_index_topk_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32]
+        L.coli_index_topk.restype = C.c_int
+        L.coli_index_topk.argtypes = [vp, C.c_int32, C.c_int32, C.c_int64, vp, C.c_int32, C.c_int32,
+                                      vp, vp, sz, vp]
         L.coli_moe_status_str.restype = C.c_char_p
         L.coli_moe_status_str.argtypes = [C.c_int]
         L.coli_moe_version.restype = C.c_int32
@@ -271,3 +302,94 @@ def coli_moe_ffn_int4(shape: Shape, x, routing: Routing, weights: WeightsInt4, y
         _check(lib().coli_moe_ffn_int4_timed(*args, *_events(events)), "coli_moe_ffn_int4_timed")
     else:
         _check(lib().coli_moe_ffn_int4(*args), "coli_moe_ffn_int4")
+
+
+# ---------------------------------------------------------------------------
+# dense FFN layers, the expert bank, index selection
+# ---------------------------------------------------------------------------
+
+@dataclass
+class DenseWeights:
+    gate: object
+    up: object
+    down: object
+
+    def c(self) -> CDenseWeights:
+        return CDenseWeights(_ptr(self.gate), _ptr(self.up), _ptr(self.down))
+
+
+def coli_moe_dense_workspace_bytes(shape: Shape) -> int:
+    cs = shape.c()
+    return lib().coli_moe_dense_workspace_bytes(C.byref(cs))
+
+
+def coli_moe_dense_ffn(shape: Shape, x, weights: DenseWeights, y, residual=None, y_bf16=None,
+                       ws=None, ws_bytes=None, stream=None) -> None:
+    cs, cw = shape.c(), weights.c()
+    _check(lib().coli_moe_dense_ffn(C.byref(cs), _ptr(x), C.byref(cw), _ptr(residual), _ptr(y),
+                                    _ptr(y_bf16), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)),
+           "coli_moe_dense_ffn")
+
+
+def _event_handle(ev, record_on=None):
+    """torch.cuda.Event (or a raw hipEvent_t int, or None) -> handle.
+
+    torch creates an event's handle when it is first recorded.  An event the
+    library will record (record_on = that stream) is recorded there once
+    first, which creates it; an event to wait for that was never recorded has
+    nothing to wait for and is passed as NULL."""
+    if ev is None or isinstance(ev, int):
+        return ev
+    if ev.cuda_event == 0:
+        if record_on is None:
+            return None
+        ev.record(record_on)
+    return ev.cuda_event
+
+
+def coli_moe_bank_fill(shape: Shape, host, bank, experts=None, int4: bool = False, group: int = 32,
+                       copy_stream=None, wait_event=None, ready_event=None) -> None:
+    """Copy the listed experts (host ints; None = all) of `host` tensors (pinned) into `bank`."""
+    n_t = 6 if int4 else 3
+    if len(host) != n_t or len(bank) != n_t:
+        raise ValueError(f"{n_t} tensors expected")
+    cs = shape.c()
+    h = (C.c_void_p * n_t)(*[_ptr(t) for t in host])
+    b = (C.c_void_p * n_t)(*[_ptr(t) for t in bank])
+    if experts is None:
+        ex, n = None, 0
+    else:
+        ex = (C.c_int32 * len(experts))(*[int(e) for e in experts])
+        n = len(experts)
+    import torch
+    cstream = copy_stream if copy_stream is not None else torch.cuda.current_stream()
+    _check(lib().coli_moe_bank_fill(C.byref(cs), 1 if int4 else 0, group, h, b, ex, n,
+                                    _stream(cstream), _event_handle(wait_event),
+                                    _event_handle(ready_event, cstream)), "coli_moe_bank_fill")
+
+
+def coli_moe_bank_acquire(compute_stream, ready_event) -> None:
+    _check(lib().coli_moe_bank_acquire(_stream(compute_stream), _event_handle(ready_event)),
+           "coli_moe_bank_acquire")
+
+
+def coli_moe_bank_release(compute_stream, free_event) -> None:
+    import torch
+    cstream = compute_stream if compute_stream is not None else torch.cuda.current_stream()
+    _check(lib().coli_moe_bank_release(_stream(cstream), _event_handle(free_event, cstream)),
+           "coli_moe_bank_release")
+
+
+def coli_index_topk_workspace_bytes(rows: int, L: int, k: int) -> int:
+    return lib().coli_index_topk_workspace_bytes(rows, L, k)
+
+
+def coli_index_topk(scores, k: int, idx, tail: int = 0, lens=None, ws=None, ws_bytes=None,
+                    stream=None, L: Optional[int] = None, ld: Optional[int] = None) -> None:
+    """scores: fp32 [rows][ld] device tensor (L columns used); idx: int32 [rows][k]."""
+    rows = scores.shape[0]
+    ld = scores.stride(0) if ld is None else ld
+    L = scores.shape[1] if L is None else L
+    _check(lib().coli_index_topk(scores.data_ptr(), rows, L, ld, _ptr(lens), k, tail, _ptr(idx),
+                                 _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)),
+           "coli_index_topk")

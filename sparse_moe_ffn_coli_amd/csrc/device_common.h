@@ -629,10 +629,11 @@ __device__ __forceinline__ int f16_chunk_slot(int e) { return (e & 3) * 2 + (e >
 // 8 nibbles of w (element p in bits 4p..4p+3) -> 8 fp16 values
 // (nibble - 8) * scale in the chunk order 0,4,1,5,2,6,3,7.  Pairs j = 0, 2
 // take the nibbles from bits 0-3 (and 16-19) of w and of w >> 8: under the
-// exponent of 1024 they read 1024 + n.  Pairs j = 1, 3 take them in place
-// from bits 4-7: 1024 + 16 n, so 1152 is subtracted and the scale divided by
-// 16 (exact: a power of two).  Either way the difference is exact and the
-// one multiply rounds the exact product (n - 8) * scale.  scale16 = scale / 16.
+// exponent of 1024 they read 1024 + n, and subtracting 1032 leaves n - 8.
+// Pairs j = 1, 3 take them in place from bits 4-7: 1024 + 16 n, and
+// (1024 + 16 n) / 16 - 72 = n - 8 (one fused multiply-add; every step is
+// exact in fp16).  Either way n - 8 is exact and the one multiply by the
+// scale rounds the exact product (n - 8) * scale, for every finite scale.
 __device__ __forceinline__ uint32_t nibble_pair(uint32_t w, uint32_t mask, uint32_t magic)
 {
     // (w & mask) | magic in one instruction (the compiler splits it in two
@@ -641,17 +642,22 @@ __device__ __forceinline__ uint32_t nibble_pair(uint32_t w, uint32_t mask, uint3
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
     return r;
 }
-__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, f16x2 scale2, f16x2 scale16)
+__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, f16x2 scale2)
 {
     const f16x2 off0 = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const f16x2 off1 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const f16x2 off1 = {(_Float16)-72.0f, (_Float16)-72.0f};
     const uint32_t w8 = w >> 8;
     const uint32_t magic = 0x64006400u;
+    auto lo = [&](uint32_t v) { return __builtin_bit_cast(f16x2, nibble_pair(v, 0x000F000Fu, magic)) - off0; };
+    auto hi = [&](uint32_t v) {
+        return __builtin_elementwise_fma(__builtin_bit_cast(f16x2, nibble_pair(v, 0x00F000F0u, magic)), sixteenth, off1);
+    };
     u32x4 r;
-    r[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w, 0x000F000Fu, magic)) - off0) * scale2);
-    r[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w, 0x00F000F0u, magic)) - off1) * scale16);
-    r[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w8, 0x000F000Fu, magic)) - off0) * scale2);
-    r[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, nibble_pair(w8, 0x00F000F0u, magic)) - off1) * scale16);
+    r[0] = __builtin_bit_cast(uint32_t, lo(w) * scale2);
+    r[1] = __builtin_bit_cast(uint32_t, hi(w) * scale2);
+    r[2] = __builtin_bit_cast(uint32_t, lo(w8) * scale2);
+    r[3] = __builtin_bit_cast(uint32_t, hi(w8) * scale2);
     return r;
 }
 
@@ -678,8 +684,10 @@ struct I4Cfg {
 
 // One tile.  I4: arow[u] is token row 8u + lane / 8 of the tile (element 0),
 // brow[j] weight row (4w + j) * 16 + lane / 4 (byte 0), w = wave, srow the
-// scales of weight row tid.  bf16 tiles: a0 + r * lda is token row r (the
-// shared expert's rows are contiguous), brow as above, srow unused.  valid:
+// scales of weight row tid.  bf16 tiles (the shared expert): a0 + r * lda
+// is token row r in bf16, natural order (the shared expert's rows are
+// contiguous), brow as above, srow unused; the products run on bf16 MFMA as
+// in the bf16 layer.  valid:
 // token rows of the tile that are real (copies of row groups wholly past
 // them are skipped; their results are dropped by the caller).
 template <class C, bool I4>
@@ -789,14 +797,12 @@ __device__ __forceinline__ void i4_mainloop(const uint16_t *const (&arow)[C::ARO
                 const int gi = (group == 32) ? 2 * blk + h
                                              : (kt * KS + 64 * blk + 32 * h) / group - kt * KS / group;
                 u32x4 bq[C::FN];
-                f16x2 sc[C::FN], sc16[C::FN];
-                const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+                f16x2 sc[C::FN];
 #pragma unroll
                 for (int n = 0; n < C::FN; ++n) {
                     const int c = 2 * blk + h;
                     bq[n] = *reinterpret_cast<const u32x4 *>(sb + br[n] * 64 + ((c ^ ((br[n] >> 2) & 3)) * 16));
                     sc[n] = fp16_bits_splat(ss[br[n] * 4 + gi]);
-                    sc16[n] = sc[n] * sixteenth;
                 }
                 f16x8 a[4];
 #pragma unroll
@@ -809,18 +815,17 @@ __device__ __forceinline__ void i4_mainloop(const uint16_t *const (&arow)[C::ARO
 #pragma unroll
                     for (int n = 0; n < C::FN; ++n)
                         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            a[j], __builtin_bit_cast(f16x8, int4x8_to_f16x8(bq[n][j], sc[n], sc16[n])), acc[n], 0, 0, 0);
+                            a[j], __builtin_bit_cast(f16x8, int4x8_to_f16x8(bq[n][j], sc[n])), acc[n], 0, 0, 0);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int c = 2 * h + j;
-                const f16x8 a = *reinterpret_cast<const f16x8 *>(sa + ar * 64 + ((c ^ ((ar >> 2) & 3)) * 16));
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sa + ar * 64 + ((c ^ ((ar >> 2) & 3)) * 16));
 #pragma unroll
                 for (int n = 0; n < C::FN; ++n) {
-                    const u32x4 braw = *reinterpret_cast<const u32x4 *>(sb + br[n] * 64 + ((c ^ ((br[n] >> 2) & 3)) * 16));
-                    acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        a, __builtin_bit_cast(f16x8, bf16x8_to_f16x8(braw)), acc[n], 0, 0, 0);
+                    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(sb + br[n] * 64 + ((c ^ ((br[n] >> 2) & 3)) * 16));
+                    acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[n], 0, 0, 0);
                 }
             }
         }

@@ -94,6 +94,18 @@ struct ExpertTile {
 
 constexpr int FIND_MAX_RUN = 16;     // experts per lane for E <= 1024
 
+// Token of row r of a tile.  The shared expert's rows (and a dense layer's,
+// which has no routed rows: R = 0) are the tokens in order; a routed row's
+// token comes from the permutation.  Every lane loads its permutation entry
+// (a clamped index for the shared expert) and the token is selected, not
+// branched on, so the loads of all rows are in flight together.
+__device__ __forceinline__ int tile_token(const ExpertTile &et, const int32_t *__restrict__ perm, int r, int R,
+                                          int K)
+{
+    const int p = (R > 0) ? perm[min(et.base + r, R - 1)] : 0;
+    return et.shared ? r : p / max(K, 1);
+}
+
 // Tile of this block for BM-row tiles and nnt column tiles.  The expert's row
 // count and first row come from the same register copy of the counts as the
 // search (the first row of expert e is the sum of the counts before it), so
@@ -108,7 +120,7 @@ __device__ __forceinline__ ExpertTile find_tile(const int32_t *__restrict__ coun
     // tiles of its run
     int cnt[FIND_MAX_RUN];
 #pragma unroll
-    for (int k = 0; k < FIND_MAX_RUN; ++k) cnt[k] = count[min(lane * run + k, E - 1)];
+    for (int k = 0; k < FIND_MAX_RUN; ++k) cnt[k] = (E > 0) ? count[min(lane * run + k, E - 1)] : 0;
     int mtk[FIND_MAX_RUN];
     int local = 0, clocal = 0;
 #pragma unroll
@@ -375,12 +387,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(
         // padding rows (past the expert's last row) reread its first row
         int r = et.m0 + a_chunk_row<C>(i);
         if (a_chunk_row<C>(i) >= C::BM || r >= et.cnt) r = et.m0;
-        // every lane loads (a clamped index for the shared expert) and the
-        // value is selected, not branched on, so the loads of all rows are
-        // in flight together
-        const int p = perm[min(et.base + r, T * K - 1)];
-        const int tok = (et.shared ? r * K : p) / K;
-        ap[i] = x + (size_t)tok * D + ch0 * 8;
+        ap[i] = x + (size_t)tile_token(et, perm, r, T * K, K) * D + ch0 * 8;
     }
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i)
@@ -553,11 +560,7 @@ __device__ __forceinline__ void gateup_big_tile(
         using S = StreamRows;
         const int row = stream_a_row(w);
         const int r = (et.m0 + row < et.cnt) ? et.m0 + row : et.m0;
-        // every lane loads (a clamped index for the shared expert) and the
-        // value is selected, not branched on, so no load waits for another
-        const int p = perm[min(et.base + r, R - 1)];
-        const int tok = (et.shared ? r * K : p) / K;
-        const uint16_t *ra = x + (size_t)tok * D + big_copy_chunk<S>(row) * 8;
+        const uint16_t *ra = x + (size_t)tile_token(et, perm, r, R, K) * D + big_copy_chunk<S>(row) * 8;
         const uint16_t *rb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -582,9 +585,7 @@ __device__ __forceinline__ void gateup_big_tile(
         const int ch = big_copy_chunk<BigCfg>(row);
         int r = et.m0 + row;                      // padding rows reread the tile's first row
         if (r >= et.cnt) r = et.m0;
-        const int p = perm[min(et.base + r, R - 1)];
-        const int tok = (et.shared ? r * K : p) / K;
-        rp[j] = x + (size_t)tok * D + ch * 8;
+        rp[j] = x + (size_t)tile_token(et, perm, r, R, K) * D + ch * 8;
         rp[BigCfg::CPO + j] = gateup_b_row(G, U, f0, row, D, F) + ch * 8;
     }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
@@ -698,9 +699,12 @@ __global__ __launch_bounds__(512) void down_big_kernel(
 // ---------------------------------------------------------------------------
 // 1'/2'. int4 routed experts: the same grouped GEMMs on the int4 engine
 // (weights dequantised from LDS as their fragments are read).  The shared
-// expert (bf16) shares the launches: its tiles run the engine's bf16 mode.
-// The A operands are fp16 in the engine's chunk order: x16 (written by
-// x_to_f16_kernel) and h16 (written by the gate+up kernel in that order).
+// expert (bf16) shares the launches: its tiles run the engine's bf16 mode on
+// x and on its hidden rows in bf16, exactly the arithmetic of the bf16
+// layer.  The routed experts' A operands are fp16 in the engine's chunk
+// order: x16 (written by x_to_f16_kernel) and h16 (written by the gate+up
+// kernel in that order; the shared expert's rows of the same buffer hold
+// bf16 in natural order).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restrict__ x, long n8,
                                                        uint16_t *__restrict__ x16)
@@ -713,7 +717,7 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restric
 
 template <class C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU))) void gateup_int4_kernel(
-    const uint16_t *__restrict__ x16, const uint8_t *__restrict__ gate_q, const uint16_t *__restrict__ gate_s,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ x16, const uint8_t *__restrict__ gate_q, const uint16_t *__restrict__ gate_s,
     const uint8_t *__restrict__ up_q, const uint16_t *__restrict__ up_s, int group,
     const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
     const int32_t *__restrict__ count, const int32_t *__restrict__ perm, int T, int D, int E, int K, int F,
@@ -744,8 +748,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
     f32x16 acc[C::FN];
     if (et.shared) {
 #pragma unroll
-        for (int u = 0; u < C::AROWS; ++u) arow[u] = x16;
-        i4_mainloop<C, false>(arow, x16 + (size_t)et.m0 * D, D, brow, nullptr, group, D, valid, lds, acc);
+        for (int u = 0; u < C::AROWS; ++u) arow[u] = x;
+        i4_mainloop<C, false>(arow, x + (size_t)et.m0 * D, D, brow, nullptr, group, D, valid, lds, acc);
     } else {
 #pragma unroll
         for (int u = 0; u < C::AROWS; ++u) {
@@ -758,16 +762,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
         i4_mainloop<C, true>(arow, nullptr, 0, brow, srow, group, D, valid, lds, acc);
     }
 
-    // h16 in the engine's chunk order: column f is stored at (f & ~7) + slot(f & 7)
-    // (fragment pair (2p, 2p + 1) = columns fo + 32 p; 32 p keeps the chunk slot)
+    // routed rows: h16 in fp16, the engine's chunk order -- column f is stored
+    // at (f & ~7) + slot(f & 7) (fragment pair (2p, 2p + 1) = columns fo + 32 p;
+    // 32 p keeps the chunk slot); the shared expert's rows: bf16, natural order
     const int wn = w % C::WAVES_N, wm = w / C::WAVES_N;
     const int fo = f0 + wn * (C::FN / 2) * 32 + (lane & 31);
-    const int fs = (fo & ~7) + f16_chunk_slot(fo & 7);
-    frag_store_rows<1, C::FN / 2>(et, h16 + fs, (size_t)F, et.base, wm * 32 + 4 * (lane >> 5), F - fo,
-                                  [&](int, int p, int i) {
-                                      return __builtin_bit_cast(
-                                          uint16_t, (_Float16)swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
-                                  });
+    const int r0 = wm * 32 + 4 * (lane >> 5);
+    if (et.shared) {
+        frag_store_rows<1, C::FN / 2>(et, h16 + fo, (size_t)F, et.base, r0, F - fo, [&](int, int p, int i) {
+            return f32_to_bf16_bits(swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
+        });
+    } else {
+        const int fs = (fo & ~7) + f16_chunk_slot(fo & 7);
+        frag_store_rows<1, C::FN / 2>(et, h16 + fs, (size_t)F, et.base, r0, F - fo, [&](int, int p, int i) {
+            return __builtin_bit_cast(uint16_t, (_Float16)swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
+        });
+    }
 }
 
 template <class C>
@@ -840,31 +850,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     // flight together: unconditional loads (slots past K reread slot K - 1;
     // they are not summed), and the empty asm statements take every loaded
     // value before any use, so the compiler cannot sink a load into a branch
-    float wj[8];
-    int iv[8];
-    u32x4 ov[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const size_t a = (size_t)t * K + min(j, K - 1);
-        wj[j] = w[a];
-        iv[j] = inv[a];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ov[j] = *reinterpret_cast<const u32x4 *>(o + (size_t)iv[j] * D + d);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(ov[j]));
     const size_t idx = (size_t)t * D + d;
     const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sx + idx);
     const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sx + idx + 4);
     float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    if (K > 0) {                                  // K = 0: a dense layer, no routed rows
+        float wj[8];
+        int iv[8];
+        u32x4 ov[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < K)
+        for (int j = 0; j < 8; ++j) {
+            const size_t a = (size_t)t * K + min(j, K - 1);
+            wj[j] = w[a];
+            iv[j] = inv[a];
+        }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                v[2 * k] = fmaf(wj[j], __uint_as_float(ov[j][k] << 16), v[2 * k]);
-                v[2 * k + 1] = fmaf(wj[j], __uint_as_float(ov[j][k] & 0xffff0000u), v[2 * k + 1]);
-            }
+        for (int j = 0; j < 8; ++j) ov[j] = *reinterpret_cast<const u32x4 *>(o + (size_t)iv[j] * D + d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(ov[j]));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    v[2 * k] = fmaf(wj[j], __uint_as_float(ov[j][k] << 16), v[2 * k]);
+                    v[2 * k + 1] = fmaf(wj[j], __uint_as_float(ov[j][k] & 0xffff0000u), v[2 * k + 1]);
+                }
+    }
     if (residual) {
         const f32x4 r0 = *reinterpret_cast<const f32x4 *>(residual + idx);
         const f32x4 r1 = *reinterpret_cast<const f32x4 *>(residual + idx + 4);
@@ -966,7 +978,10 @@ static_assert(I4Cfg<64>::BN == TILE_N && I4Cfg<32>::BN == TILE_N && BigCfg::BN =
 
 int ffn_tile_rows(int T, int E, int K, int int4)
 {
-    // rows per expert on average decides the tile height
+    // a dense layer (K = 0: no experts, T rows of one weight set) takes the
+    // 256-row tiles from 512 rows on; otherwise rows per expert on average
+    // decides the tile height
+    if (K == 0) return T >= 512 ? BIG_BM : SMALL_BM;
     const long R = (long)T * K;
     if (R <= 24L * E) return SMALL_BM;
     return int4 ? I4Cfg<64>::BM : BIG_BM;
@@ -1037,7 +1052,7 @@ static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t s
     x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint16_t *)a.x, n8, a.x16);
     mk.mark(st);                                     // the gate+up stage is its kernel alone
     gateup_int4_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
-        a.x16, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
+        (const uint16_t *)a.x, a.x16, a.gate_q, a.gate_s, a.up_q, a.up_s, a.group,
         (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.perm,
         a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
     mk.mark(st);

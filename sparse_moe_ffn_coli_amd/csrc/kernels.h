@@ -60,6 +60,8 @@ struct FfnLaunch {
 };
 
 hipError_t launch_route(const RouteLaunch &a, hipStream_t st);
+hipError_t launch_index_topk(const float *scores, int rows, int L, long ld, const int32_t *lens, int k, int tail,
+                             int32_t *idx, hipStream_t st);
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st);
 
 int perm_tiles(int T);

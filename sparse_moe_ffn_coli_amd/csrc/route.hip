@@ -340,13 +340,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
     // logit = (split 0 + split 1 + ...) + bias; 0 marks an empty slot, every
     // real logit maps above 0 (NaN aside).  Every partial and bias of the
     // token is loaded before any sum, so the loads cost one memory latency:
-    // the loads are unconditional (the last slot's index clamped to a real
-    // expert, splits past the last clamped to it), and the empty asm
+    // the loads are unconditional (every slot's index clamped to a real
+    // expert -- the slot count is rounded up to a template size, so slots
+    // before the last may lie past E as well -- and splits past the last
+    // clamped to it), and the empty asm
     // statements take every loaded value before any is used, so the compiler
-    // cannot sink a load into a branch.  Slot s of lane l is expert 64 s + l,
-    // at a constant offset from the lane's first, so one address serves a row.
+    // cannot sink a load into a branch.  Slot s of lane l is expert 64 s + l
+    // (clamped), so every load of a row is addressed from the row's pointer.
     float part[SLOTS][NSP], bs[SLOTS];
-    auto col = [&](int s) { return (s < SLOTS - 1) ? lane + 64 * s : min(lane + 64 * s, E - 1); };
+    auto col = [&](int s) { return min(lane + 64 * s, E - 1); };
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) bs[s] = bias[col(s)];
 #pragma unroll

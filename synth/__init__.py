@@ -17,6 +17,18 @@ expert width 768 are the workload definition's, the pages do not give them):
   stacked  T=256,  D=2048, F=768, bf16, 42 layers with independent weights
   int4_decode  T=64, D=2048, F=768, int4 experts as in int4 (decode batch)
 
+Dense FFN layers (the model's first layers run a dense FFN, same section):
+  dense_decode   T=64,   D=2048, F=6912, bf16
+  dense_prefill  T=4096, D=2048, F=6912, bf16
+(the pages give no dense width; 6912 = 9 x 768 is the hidden width a token
+activates in an MoE layer: 8 routed experts and the shared one.)
+
+Index selection of the sparse attention ("MLA/DSA": top-2048 of the indexer
+scores, the last kpool = 4 tokens always kept), fp32 scores ~ N(0, 1):
+  index_topk         2048 query rows (a prefill chunk) over a 32768-entry
+                     cache, causal: row i sees its first 30721 + i entries
+  index_topk_decode  64 query rows, each over a full 32768-entry cache
+
 Value recipe: x ~ N(0,1); router, gate, up ~ N(0, 1/D); down ~ N(0, 1/F);
 shared expert likewise; seed 0.  Token rows can be redrawn ("attempts") so
 that the gap between the 8th and 9th router probability exceeds 1e-3; the
@@ -41,6 +53,7 @@ GAP_ATTEMPTS_PATH = os.path.join(_ROOT, "tests", "golden", "gap_attempts.json")
 # tensor ids of the random streams
 X, WR, BIAS, GATE, UP, DOWN, SGATE, SUP, SDOWN = 1, 2, 3, 4, 5, 6, 7, 8, 9
 GATE_Q, UP_Q, DOWN_Q, GATE_S, UP_S, DOWN_S = 10, 11, 12, 13, 14, 15
+DGATE, DUP, DDOWN, SCORES = 16, 17, 18, 19
 
 CONFIGS = {
     "tiny": dict(cid=1, T=8, D=128, E=288, K=8, F=64, dtype="f32", bias="uniform",
@@ -55,6 +68,14 @@ CONFIGS = {
                     layers=42, int4=False),
     "int4_decode": dict(cid=6, T=64, D=2048, E=288, K=8, F=768, dtype="bf16", bias="uniform",
                         layers=1, int4=True, group=32),
+}
+DENSE_CONFIGS = {
+    "dense_decode": dict(cid=7, T=64, D=2048, F=6912, dtype="bf16"),
+    "dense_prefill": dict(cid=8, T=4096, D=2048, F=6912, dtype="bf16"),
+}
+INDEX_CONFIGS = {
+    "index_topk": dict(cid=9, rows=2048, L=32768, k=2048, tail=4, lens="causal"),
+    "index_topk_decode": dict(cid=10, rows=64, L=32768, k=2048, tail=4, lens="full"),
 }
 ZIPF_S = 1.1
 GAP_MIN = 1e-3
@@ -206,3 +227,24 @@ def bf16_bits(v: float) -> int:
 
 def fp16_bits(v: float) -> int:
     return lib().synth_fp16(v)
+
+
+def dense_weights(cfg: dict, layer: int = 0, seed: int = 0) -> dict:
+    """gate, up [F][D] ~ N(0, 1/D) and down [D][F] ~ N(0, 1/F) of a dense FFN layer, plus x."""
+    D, F, dt = cfg["D"], cfg["F"], cfg["dtype"]
+    sd, sf = 1.0 / math.sqrt(D), 1.0 / math.sqrt(F)
+    return dict(gate=normal(key(cfg, layer, DGATE, seed), F, D, sd, dt),
+                up=normal(key(cfg, layer, DUP, seed), F, D, sd, dt),
+                down=normal(key(cfg, layer, DDOWN, seed), D, F, sf, dt),
+                x=x_rows(cfg, None, layer, seed))
+
+
+def index_scores(cfg: dict, seed: int = 0):
+    """fp32 scores [rows][L] ~ N(0, 1) and the per-row valid lengths."""
+    rows, L = cfg["rows"], cfg["L"]
+    scores = normal(key(cfg, 0, SCORES, seed), rows, L, 1.0, "f32")
+    if cfg["lens"] == "causal":
+        lens = (L - rows + 1 + np.arange(rows)).astype(np.int32)
+    else:
+        lens = np.full(rows, L, np.int32)
+    return scores, lens

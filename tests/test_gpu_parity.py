@@ -1,13 +1,12 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
 inputs: small shapes that span several tiles with ragged tails, the full
-workloads (prefill on sampled tokens), edge cases, and run-to-run bitwise
-determinism.  Tolerances are in gpu_helpers."""
+workloads (every token), edge cases, and run-to-run bitwise determinism.
+Tolerances are in gpu_helpers."""
 import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import (compare, custom_cfg, gpu_layer, make_inputs, run_gpu, run_oracle,
-                         sample_tokens)
+from gpu_helpers import compare, custom_cfg, gpu_layer, make_inputs, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -73,23 +72,14 @@ def test_decode_bf16():
     _report("decode", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="decode"))
 
 
-def test_prefill_bf16_sampled():
-    import oracle
+def test_prefill_bf16_every_token():
     cfg = synth.CONFIGS["prefill"]
     W = synth.workload("prefill")
     got = run_gpu(W, cfg)
-    T, D, E, K = cfg["T"], cfg["D"], cfg["E"], cfg["K"]
-    # routing of every token from the oracle, the FFN for a sample
-    z = oracle.router_logits(W["x"], W["wr"], W["bias"], T, D, E)
-    ids, w = oracle.select_topk(z, K)
-    count, offset, perm, inv = oracle.permutation(ids, E)
-    assert (count == 0).sum() > 0
-    toks = sample_tokens(ids, count, T)
-    y = oracle.moe_ffn(W["x"], ids, w, W["gate"], W["up"], W["down"], W["s_gate"], W["s_up"],
-                       W["s_down"], T, D, E, K, cfg["F"], tokens=toks)
-    ref = dict(ids=ids, w=w, count=count, offset=offset, perm=perm, inv=inv, y=y)
-    err = compare(got, ref, cfg, tokens=toks, label="prefill")
-    _report(f"prefill ({len(toks)} sampled tokens, {(count > 0).sum()} non-empty experts)", err)
+    ref = run_oracle(W, cfg)
+    assert (ref["count"] == 0).sum() > 0
+    err = compare(got, ref, cfg, label="prefill")
+    _report(f"prefill (all {cfg['T']} tokens, {(ref['count'] > 0).sum()} non-empty experts)", err)
 
 
 # ---------------------------------------------------------------------------
@@ -106,23 +96,11 @@ def test_int4_small_shapes(cid, T, D, E, K, F, group):
     _report(f"int4 cid={cid}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label=f"int4 cid={cid}"))
 
 
-def test_int4_workload_sampled():
-    import oracle
+def test_int4_workload_every_token():
     cfg = synth.CONFIGS["int4"]
     W = synth.workload("int4")
-    got = run_gpu(W, cfg)
-    T, D, E, K, F, G = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], cfg["group"]
-    z = oracle.router_logits(W["x"], W["wr"], W["bias"], T, D, E)
-    ids, w = oracle.select_topk(z, K)
-    count, offset, perm, inv = oracle.permutation(ids, E)
-    toks = sample_tokens(ids, count, T)
-    Mi = oracle.Mat.int4
-    y = oracle.moe_ffn(W["x"], ids, w, Mi(W["gate_q"], W["gate_s"], G), Mi(W["up_q"], W["up_s"], G),
-                       Mi(W["down_q"], W["down_s"], G), W["s_gate"], W["s_up"], W["s_down"],
-                       T, D, E, K, F, tokens=toks)
-    ref = dict(ids=ids, w=w, count=count, offset=offset, perm=perm, inv=inv, y=y)
-    _report(f"int4 workload ({len(toks)} sampled tokens)",
-            compare(got, ref, cfg, tokens=toks, label="int4"))
+    _report(f"int4 workload (all {cfg['T']} tokens)",
+            compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4"))
 
 
 def test_int4_decode():
@@ -132,27 +110,32 @@ def test_int4_decode():
     _report("int4 decode", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4 decode"))
 
 
-def test_int4_stacked_layer_shape_sampled():
+def test_int4_stacked_layer_shape_every_token():
     # one layer of the stacked decode shape (T = 256) with int4 experts; tokens and
     # router are the stacked workload's first layer, whose stored redraws keep the
     # 8th and 9th router probabilities apart
-    import oracle
     cfg = dict(synth.CONFIGS["stacked"], layers=1, int4=True, group=32)
     W = synth.layer_weights(cfg, 0)
     W["x"] = synth.x_rows(cfg, synth.load_attempts("stacked"))
-    got = run_gpu(W, cfg)
-    T, D, E, K, F, G = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], cfg["group"]
-    z = oracle.router_logits(W["x"], W["wr"], W["bias"], T, D, E)
-    ids, w = oracle.select_topk(z, K)
-    count, offset, perm, inv = oracle.permutation(ids, E)
-    toks = sample_tokens(ids, count, T)
-    Mi = oracle.Mat.int4
-    y = oracle.moe_ffn(W["x"], ids, w, Mi(W["gate_q"], W["gate_s"], G), Mi(W["up_q"], W["up_s"], G),
-                       Mi(W["down_q"], W["down_s"], G), W["s_gate"], W["s_up"], W["s_down"],
-                       T, D, E, K, F, tokens=toks)
-    ref = dict(ids=ids, w=w, count=count, offset=offset, perm=perm, inv=inv, y=y)
-    _report(f"int4 stacked-layer shape ({len(toks)} sampled tokens)",
-            compare(got, ref, cfg, tokens=toks, label="int4 T=256"))
+    _report("int4 stacked-layer shape (all 256 tokens)",
+            compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4 T=256"))
+
+
+def test_int4_small_scales():
+    # group scales in [2^-14, 2^-12), where a scale divided by 16 would be an fp16
+    # subnormal: each weight must still be (nibble - 8) * scale rounded once.  The
+    # tokens are scaled by 128 (exact in bf16) so the products keep their size, and
+    # the shared expert is zero so that y is the routed experts' output alone.
+    cfg = custom_cfg(134, 90, 256, 24, 8, 128, "bf16", int4=True, group=32)
+    W = make_inputs(cfg)
+    rng = np.random.default_rng(134)
+    for k in ("gate_s", "up_s", "down_s"):
+        W[k] = rng.integers(0x0400, 0x0C00, size=W[k].shape, dtype=np.uint16)
+    for k in ("s_gate", "s_up", "s_down"):
+        W[k] = np.zeros_like(W[k])
+    x32 = (W["x"].astype(np.uint32) << 16).view(np.float32) * np.float32(128.0)
+    W["x"] = (x32.view(np.uint32) >> 16).astype(np.uint16)
+    _report("int4 small scales", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4 small scales"))
 
 
 # ---------------------------------------------------------------------------
@@ -168,6 +151,10 @@ def test_int4_stacked_layer_shape_sampled():
     # almost every thread's four experts, K = 6 leaves rows per tile uneven
     (116, 1500, 64, 1000, 8, 64, "bf16"),
     (117, 2100, 64, 288, 6, 64, "bf16"),
+    # expert counts whose top-K slot count is rounded up to the next kernel size
+    # (6 slots run as 8, 10 as 16): every slot's loads stay inside the logits and bias
+    (118, 40, 64, 330, 8, 64, "bf16"),
+    (119, 40, 64, 600, 8, 64, "bf16"),
 ])
 def test_edge_shapes(cid, T, D, E, K, F, dt):
     cfg = custom_cfg(cid, T, D, E, K, F, dt)
@@ -189,24 +176,35 @@ def test_zero_tokens():
 
 
 def test_residual_and_bf16_output():
+    # y = residual + layer(x) written in place over the residual, and its bf16 copy:
+    # y against the oracle given the same residual, y_bf16 against the oracle's
+    # round-to-nearest-even of the GPU's fp32 y
+    import oracle
     import torch
     cfg = custom_cfg(121, 80, 128, 32, 8, 64, "bf16")
     W = make_inputs(cfg)
     layer, x = gpu_layer(W, cfg)
-    y0 = layer(x).clone()
-    res = torch.randn_like(y0)
-    y = res.clone()
-    yb = torch.empty(y0.shape, dtype=torch.bfloat16, device=y0.device)
-    layer.ffn(x, y=y, residual=y, y_bf16=yb)          # in place: y = y + layer(x)
+    res = np.random.default_rng(121).standard_normal((cfg["T"], cfg["D"])).astype(np.float32) * 3
+    y = torch.from_numpy(res.copy()).cuda()
+    yb = torch.empty(y.shape, dtype=torch.bfloat16, device=y.device)
+    layer(x, y=y, residual=y, y_bf16=yb)
     torch.cuda.synchronize()
-    assert torch.equal(y, res + y0)
-    assert torch.equal(yb, y.to(torch.bfloat16))
+    got = layer.routing_numpy()
+    got["y"] = y.cpu().numpy().astype(np.float64)
+    g, u, d = W["gate"], W["up"], W["down"]
+    ref = oracle.moe_layer(W["x"], W["wr"], W["bias"], g, u, d, W["s_gate"], W["s_up"], W["s_down"],
+                           cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"], residual=res.astype(np.float64))
+    _report("residual in place", compare(got, ref, cfg, label="residual"))
+    yf = y.cpu().numpy().reshape(-1)
+    ybits = yb.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    want = np.array([oracle.bf16_from_double(float(v)) for v in yf], dtype=np.uint16)
+    assert np.array_equal(ybits, want), "y_bf16 is not y rounded to nearest even"
 
 
 # ---------------------------------------------------------------------------
 # determinism: identical inputs give bitwise identical routing and outputs
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "int4", "int4_decode"])
 def test_bitwise_determinism(name):
     import torch
     cfg = synth.CONFIGS[name]
