@@ -201,6 +201,24 @@ coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
                                     size_t ws_bytes, void *stream, void *const *events,
                                     int32_t n_events);
 
+/* ---- an FFN call that allocates nothing ----------------------------------
+ * For callers that cannot allocate device memory or hand over a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): coli_moe_ffn with its workspace taken from a scratch array
+ * the library keeps in each GPU's memory (COLI_NOALLOC_SCRATCH_BYTES, held
+ * by every GPU the library runs on until the process ends).  A shape whose
+ * coli_moe_workspace_bytes(s, 0) exceeds the array returns COLI_E_WORKSPACE
+ * before anything is enqueued (the array holds T up to about 540 tokens at
+ * D = 2048, F = 768, K = 8).  Every call on one GPU uses the same array:
+ * calls that overlap in time on one GPU (other streams, or host threads
+ * without an order between their calls) race and give undefined results.
+ * Nothing in the array has to start at zero; each call writes every byte it
+ * later reads.  Results are bitwise those of coli_moe_ffn. */
+#define COLI_NOALLOC_SCRATCH_BYTES (32u << 20)
+coli_status coli_moe_ffn_noalloc(const coli_moe_shape *s, const void *x, const coli_moe_routing *r,
+                                 const coli_moe_weights *w, const float *residual, float *y,
+                                 void *y_bf16, void *stream);
+
 /* ---- dense FFN layers ----------------------------------------------------
  * The model's first layers run a dense FFN instead of the experts
  * ([glm5next] "Architecture": layers 0-2 dense FFN only; "MoE FFN": dense FFN

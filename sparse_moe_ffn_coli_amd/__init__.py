@@ -42,7 +42,7 @@ EXPORTED = ("coli_moe_workspace_bytes", "coli_moe_route", "coli_moe_ffn", "coli_
             "coli_moe_route_timed", "coli_moe_ffn_timed", "coli_moe_ffn_int4_timed",
             "coli_moe_dense_workspace_bytes", "coli_moe_dense_ffn",
             "coli_moe_bank_fill", "coli_moe_bank_acquire", "coli_moe_bank_release",
-            "coli_index_topk_workspace_bytes", "coli_index_topk",
+            "coli_index_topk_workspace_bytes", "coli_index_topk", "coli_moe_ffn_noalloc",
             "coli_moe_status_str", "coli_moe_version")
 ROUTE_STAGES = ("router", "topk", "perm")
 FFN_STAGES = ("gate_up", "down", "combine")
@@ -132,6 +132,9 @@ def lib():
         L.coli_index_topk.restype = C.c_int
         L.coli_index_topk.argtypes = [vp, C.c_int32, C.c_int32, C.c_int64, vp, C.c_int32, C.c_int32,
                                       vp, vp, sz, vp]
+        L.coli_moe_ffn_noalloc.restype = C.c_int
+        L.coli_moe_ffn_noalloc.argtypes = [sp, vp, C.POINTER(CRouting), C.POINTER(CWeights), vp, vp,
+                                           vp, vp]
         L.coli_moe_status_str.restype = C.c_char_p
         L.coli_moe_status_str.argtypes = [C.c_int]
         L.coli_moe_version.restype = C.c_int32
@@ -393,3 +396,14 @@ def coli_index_topk(scores, k: int, idx, tail: int = 0, lens=None, ws=None, ws_b
     _check(lib().coli_index_topk(scores.data_ptr(), rows, L, ld, _ptr(lens), k, tail, _ptr(idx),
                                  _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)),
            "coli_index_topk")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def coli_moe_ffn_noalloc(shape: Shape, x, routing: Routing, weights: Weights, y, residual=None,
+                         y_bf16=None, stream=None) -> None:
+    """coli_moe_ffn with the library's own per-GPU scratch array as workspace."""
+    cs, cr, cw = shape.c(), routing.c(), weights.c()
+    _check(lib().coli_moe_ffn_noalloc(C.byref(cs), _ptr(x), C.byref(cr), C.byref(cw), _ptr(residual),
+                                      _ptr(y), _ptr(y_bf16), _stream(stream)), "coli_moe_ffn_noalloc")

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/coli_moe.h"
 #include "kernels.h"
@@ -161,6 +162,33 @@ int memory_kind(const void *p)
     if (at.type == hipMemoryTypeDevice) return 1;
     if (at.type == hipMemoryTypeHost) return 2;
     return 0;
+}
+
+// ---- the scratch array of coli_moe_ffn_noalloc --------------------------------
+// Callers that cannot allocate get the FFN workspace from this array: one
+// copy per GPU, held until the process ends.  In host code `scratch` is only
+// a handle: its device address is looked up once per device (with that
+// device current) and kept in scratch_ptr, which is what kernels receive.
+static __device__ __attribute__((aligned(256))) char scratch[COLI_NOALLOC_SCRATCH_BYTES];
+
+std::mutex scratch_mu;
+void *scratch_ptr[64];
+
+coli_status scratch_for_current_device(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return COLI_E_DEVICE;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return COLI_E_DEVICE;
+        }
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return COLI_OK;
 }
 
 }  // namespace
@@ -529,6 +557,19 @@ coli_status coli_index_topk(const float *scores, int32_t rows, int32_t L, int64_
     return coli::launch_index_topk(scores, rows, L, (long)ld, lens, k, tail, idx, (hipStream_t)stream) == hipSuccess
                ? COLI_OK
                : COLI_E_LAUNCH;
+}
+
+coli_status coli_moe_ffn_noalloc(const coli_moe_shape *s, const void *x, const coli_moe_routing *r,
+                                 const coli_moe_weights *w, const float *residual, float *y, void *y_bf16,
+                                 void *stream)
+{
+    coli_status st = check_shape(s);
+    if (st != COLI_OK) return st;
+    if (ffn_ws(s, 0).total > (size_t)COLI_NOALLOC_SCRATCH_BYTES) return COLI_E_WORKSPACE;
+    if ((st = check_device()) != COLI_OK) return st;
+    void *ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != COLI_OK) return st;
+    return coli_moe_ffn(s, x, r, w, residual, y, y_bf16, ws, COLI_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -184,6 +184,18 @@ def test_int4_alias_checks_cover_every_weight():
 
 
 @no_gpu
+def test_noalloc_rejects_shapes_beyond_its_scratch_array():
+    big = _shape(T=4096)
+    assert pkg.coli_moe_workspace_bytes(big) > pkg.NOALLOC_SCRATCH_BYTES
+    cs = big.c()
+    assert pkg.lib().coli_moe_ffn_noalloc(C.byref(cs), fake(1), C.byref(_routing()), C.byref(_weights()),
+                                          None, fake(5), None, None) == E_WS
+    cs = _shape(T=64).c()                                            # fits: reaches the device query
+    assert pkg.lib().coli_moe_ffn_noalloc(C.byref(cs), fake(1), C.byref(_routing()), C.byref(_weights()),
+                                          None, fake(5), None, None) == E_DEVICE
+
+
+@no_gpu
 def test_int4_rejects_bad_groups():
     cs = _shape().c()
     for g in (0, 16, 48, 4096):
