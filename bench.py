@@ -13,8 +13,13 @@ Prints ONE JSON line.  Besides the throughput it reports
                 events recorded around that kernel inside the timed region;
   cpu_baseline: the CPU oracle timed on a bounded sample of the same inputs.
 
+The default run (prefill) also measures, as extra keys of the same line: the
+decode batch, the int4 workloads, the 42-layer stacked pass, the dense FFN
+layers, the index top-k selection and the stacked shape with its experts
+streamed through two device banks (--quick skips them).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|int4|int4_decode|stacked|tiny]
-                [--tokens T]
+                [--tokens T] [--quick]
 """
 import argparse
 import csv
@@ -265,24 +270,38 @@ def run_workload(name, steps, warmup, hip, tokens=None):
         stage_us[nm] = sum(hip.elapsed_ms(evs[(n_r + n_f) * i + o + j],
                                           evs[(n_r + n_f) * i + o + j + 1])
                            for i in range(steps)) / steps * 1e3
-    # timed region: K steps; the library records events around the gate+up
-    # kernel of every step (ffn stage 0) on the stream it launches on
-    gu = hip.events(2 * steps)
-    start, stop = hip.events(2)
+    # timed region: K steps, events only at the step boundaries
+    marks = hip.events(steps + 1)
     torch.cuda.synchronize()
     h0 = time.perf_counter()
-    hip.record(start, stream)
+    hip.record(marks[0], stream)
     for i in range(steps):
-        layer(x, ffn_events=[gu[2 * i], gu[2 * i + 1]])
-    hip.record(stop, stream)
+        layer(x)
+        hip.record(marks[i + 1], stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
-    total_ms = hip.elapsed_ms(start, stop)
-    gu_ms = [hip.elapsed_ms(gu[2 * i], gu[2 * i + 1]) for i in range(steps)]
+    total_ms = hip.elapsed_ms(marks[0], marks[steps])
+    step_ms = [hip.elapsed_ms(marks[i], marks[i + 1]) for i in range(steps)]
     log(f"{name}: {steps} timed steps, {total_ms / steps * 1e3:.1f} us/step "
         f"(host clock {host_s / steps * 1e6:.1f} us/step)")
+    # the same K steps again with the library recording events around the
+    # gate+up kernel of every step (ffn stage 0) on the stream it launches on:
+    # the dominant kernel's duration for the roofline (recording events
+    # between kernels costs a few microseconds per step, so the step time
+    # above comes from the pass without them)
+    gu = hip.events(2 * steps)
+    marks2 = hip.events(2)
+    hip.record(marks2[0], stream)
+    for i in range(steps):
+        layer(x, ffn_events=[gu[2 * i], gu[2 * i + 1]])
+    hip.record(marks2[1], stream)
+    torch.cuda.synchronize()
+    instr_ms = hip.elapsed_ms(marks2[0], marks2[1])
+    gu_ms = [hip.elapsed_ms(gu[2 * i], gu[2 * i + 1]) for i in range(steps)]
+    log(f"{name}: instrumented pass {instr_ms / steps * 1e3:.1f} us/step, gate+up "
+        f"{sum(gu_ms) / steps * 1e3:.1f} us")
 
-    hip.destroy(gu + evs + [start, stop])
+    hip.destroy(gu + evs + marks + marks2)
 
     count = layer.routing.count.cpu().numpy()
     st, flops, nbytes, n_e = algorithmic(cfg, count, int4=cfg.get("int4", False))
@@ -290,7 +309,9 @@ def run_workload(name, steps, warmup, hip, tokens=None):
     gu_s = sum(gu_ms) / len(gu_ms) / 1e3
     peak = PEAK_FP32_FLOPS if cfg["dtype"] == "f32" else PEAK_BF16_FLOPS
     res = dict(
-        cfg=cfg, step_s=step_s, host_step_s=host_s / steps, tokens_per_s=T / step_s, n_e=n_e,
+        name=name, cfg=cfg, step_s=step_s, host_step_s=host_s / steps, tokens_per_s=T / step_s, n_e=n_e,
+        step_median_s=float(np.median(step_ms)) / 1e3, step_min_s=min(step_ms) / 1e3,
+        step_instrumented_s=instr_ms / steps / 1e3,
         flops=flops, bytes=nbytes, gu_s=gu_s, stage_us={k: round(v, 2) for k, v in stage_us.items()},
         roofline=roofline(st["gate_up"]["flops"], st["gate_up"]["bytes"], gu_s, peak),
         gate_up_work=st["gate_up"],
@@ -342,18 +363,22 @@ def run_stacked(steps, warmup, hip):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    gu = hip.events(2 * L * steps)
-    start, stop = hip.events(2)
+    marks = hip.events(steps + 1)
     h0 = time.perf_counter()
-    hip.record(start, stream)
+    hip.record(marks[0], stream)
     for i in range(steps):
-        step(gu[2 * L * i:2 * L * (i + 1)])
-    hip.record(stop, stream)
+        step()
+        hip.record(marks[i + 1], stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
-    total_ms = hip.elapsed_ms(start, stop)
+    total_ms = hip.elapsed_ms(marks[0], marks[steps])
+    step_ms = [hip.elapsed_ms(marks[i], marks[i + 1]) for i in range(steps)]
+    gu = hip.events(2 * L * steps)                  # instrumented pass: the gate+up kernels
+    for i in range(steps):
+        step(gu[2 * L * i:2 * L * (i + 1)])
+    torch.cuda.synchronize()
     gu_ms = [hip.elapsed_ms(gu[2 * j], gu[2 * j + 1]) for j in range(L * steps)]
-    hip.destroy(gu + [start, stop])
+    hip.destroy(gu + marks)
     step_s = total_ms / steps / 1e3
     log(f"stacked: {steps} timed steps, {step_s * 1e3:.3f} ms per 42-layer pass")
 
@@ -365,7 +390,9 @@ def run_stacked(steps, warmup, hip):
         gu_flops, gu_bytes = gu_flops + st["gate_up"]["flops"], gu_bytes + st["gate_up"]["bytes"]
         n_es.append(n_e)
     gu_s = sum(gu_ms) / len(gu_ms) / 1e3
-    res = dict(cfg=cfg, step_s=step_s, host_step_s=host_s / steps, tokens_per_s=T / step_s,
+    res = dict(name="stacked", cfg=cfg, step_s=step_s, host_step_s=host_s / steps, tokens_per_s=T / step_s,
+               step_median_s=float(np.median(step_ms)) / 1e3, step_min_s=min(step_ms) / 1e3,
+               step_instrumented_s=None,
                n_e=round(sum(n_es) / len(n_es), 1), flops=flops, bytes=nbytes, gu_s=gu_s,
                stage_us={}, roofline=roofline(gu_flops / L, gu_bytes / L, gu_s, PEAK_BF16_FLOPS),
                gate_up_work=dict(flops=gu_flops // L, bytes=gu_bytes // L),
@@ -375,6 +402,188 @@ def run_stacked(steps, warmup, hip):
     del layers
     torch.cuda.empty_cache()
     return res
+
+
+# ---------------------------------------------------------------------------
+# the rows around the MoE layer: dense FFN layers, index selection, and the
+# stacked workload with its experts streamed through two device banks
+# ---------------------------------------------------------------------------
+def _timed_calls(fn, steps, warmup, hip, stream):
+    """Run fn() warmup times, then `steps` times between HIP events; returns
+    the per-call durations in seconds."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    marks = hip.events(steps + 1)
+    hip.record(marks[0], stream)
+    for i in range(steps):
+        fn()
+        hip.record(marks[i + 1], stream)
+    torch.cuda.synchronize()
+    out = [hip.elapsed_ms(marks[i], marks[i + 1]) / 1e3 for i in range(steps)]
+    hip.destroy(marks)
+    return out
+
+
+def _summary(times):
+    import numpy as np
+    return dict(mean_s=sum(times) / len(times), median_s=float(np.median(times)), min_s=min(times))
+
+
+def run_dense(name, steps, warmup, hip):
+    import torch
+
+    import synth
+    from sparse_moe_ffn_coli_amd import (COLI_BF16, DenseWeights, Shape, coli_moe_dense_ffn,
+                                         coli_moe_dense_workspace_bytes)
+    from sparse_moe_ffn_coli_amd.layer import to_device
+
+    cfg = synth.DENSE_CONFIGS[name]
+    T, D, F = cfg["T"], cfg["D"], cfg["F"]
+    W = synth.dense_weights(cfg)
+    shape = Shape(T, D, 0, 0, F, COLI_BF16)
+    w = DenseWeights(to_device(W["gate"]), to_device(W["up"]), to_device(W["down"]))
+    x = to_device(W["x"])
+    ws = torch.empty(coli_moe_dense_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    t = _summary(_timed_calls(lambda: coli_moe_dense_ffn(shape, x, w, y, ws=ws), steps, warmup, hip, stream))
+    flops = 2 * T * D * F * 3
+    nbytes = 3 * F * D * 2 + T * D * 2 + T * D * 4
+    log(f"{name}: {t['mean_s'] * 1e6:.1f} us per layer")
+    return {"workload": f"dense FFN layer T={T}, D={D}, F={F}, bf16", "tokens_per_s": round(T / t["mean_s"], 1),
+            "us_per_layer": round(t["mean_s"] * 1e6, 2), "us_median": round(t["median_s"] * 1e6, 2),
+            "us_min": round(t["min_s"] * 1e6, 2),
+            "roofline": roofline(flops, nbytes, t["mean_s"], PEAK_BF16_FLOPS),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+
+
+def run_index_topk(name, steps, warmup, hip):
+    import torch
+
+    import synth
+    from sparse_moe_ffn_coli_amd import coli_index_topk
+
+    cfg = synth.INDEX_CONFIGS[name]
+    rows, L, k, tail = cfg["rows"], cfg["L"], cfg["k"], cfg["tail"]
+    scores, lens = synth.index_scores(cfg)
+    s = torch.from_numpy(scores).cuda()
+    ln = torch.from_numpy(lens).cuda()
+    idx = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    t = _summary(_timed_calls(lambda: coli_index_topk(s, k, idx, tail=tail, lens=ln), steps, warmup, hip, stream))
+    nbytes = int(lens.astype("int64").sum()) * 4 + rows * 4 + rows * k * 4    # scores read, lens, idx written
+    log(f"{name}: {t['mean_s'] * 1e6:.1f} us per call")
+    return {"workload": f"index top-{k} (tail {tail}) over {rows} rows x {L} scores, fp32, "
+                        f"{'causal' if cfg['lens'] == 'causal' else 'full'} lengths",
+            "rows_per_s": round(rows / t["mean_s"], 1), "us_per_call": round(t["mean_s"] * 1e6, 2),
+            "us_median": round(t["median_s"] * 1e6, 2), "us_min": round(t["min_s"] * 1e6, 2),
+            "roofline": dict(roofline(0, nbytes, t["mean_s"], PEAK_FP32_FLOPS), algorithmic_bytes=nbytes)}
+
+
+def run_bank_stream(hip, layers=4, host_layers=2):
+    """The stacked decode shape with every layer's routed experts copied from
+    pinned host memory into one of two device banks while the previous layer
+    computes (copy stream + events).  Reports the copy alone, the compute
+    alone (same layers, weights already in the banks) and the two overlapped."""
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_moe_ffn_coli_amd import (COLI_BF16, Routing, Shape, Weights, coli_moe_bank_acquire,
+                                         coli_moe_bank_fill, coli_moe_bank_release, coli_moe_ffn,
+                                         coli_moe_route, coli_moe_workspace_bytes)
+    from sparse_moe_ffn_coli_amd.layer import to_device
+
+    cfg = synth.CONFIGS["stacked"]
+    T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
+    shape = Shape(T, D, E, K, F, COLI_BF16)
+    t0 = time.time()
+    host, dev = [], []
+    for l in range(host_layers):
+        W = synth.layer_weights(cfg, l)
+        hl = []
+        for k in ("gate", "up", "down"):
+            a = torch.from_numpy(W[k].view(np.int16))
+            p = torch.empty(a.shape, dtype=torch.int16, pin_memory=True)
+            p.copy_(a)
+            hl.append(p)
+        host.append(hl)
+        dev.append({k: to_device(W[k]) for k in ("wr", "bias", "s_gate", "s_up", "s_down")})
+        del W
+    log(f"bank stream: {host_layers} host layers pinned ({time.time() - t0:.0f}s)")
+    banks = [[torch.empty(h.shape, dtype=torch.int16, device="cuda") for h in host[0]] for _ in range(2)]
+    ready = [torch.cuda.Event() for _ in range(2)]
+    free = [torch.cuda.Event() for _ in range(2)]
+    copy = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    ws = torch.empty(coli_moe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    routing = Routing.empty(T, E, K)
+    x = to_device(synth.x_rows(cfg, synth.load_attempts("stacked")))
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    layer_bytes = sum(h.numel() * 2 for h in host[0])
+
+    def layer_compute(l):
+        d, b = dev[l % host_layers], banks[l % 2]
+        coli_moe_route(shape, x, d["wr"], d["bias"], routing, ws)
+        coli_moe_ffn(shape, x, routing, Weights(b[0], b[1], b[2], d["s_gate"], d["s_up"], d["s_down"]), y, ws=ws)
+
+    def fill(l, used):
+        coli_moe_bank_fill(shape, host[l % host_layers], banks[l % 2], copy_stream=copy,
+                           wait_event=free[l % 2] if used[l % 2] else None, ready_event=ready[l % 2])
+
+    def streamed():
+        used = [False, False]
+        fill(0, used)
+        for l in range(layers):
+            if l + 1 < layers:
+                fill(l + 1, used)
+            coli_moe_bank_acquire(compute, ready[l % 2])
+            layer_compute(l)
+            coli_moe_bank_release(compute, free[l % 2])
+            used[l % 2] = True
+
+    def copies_only():
+        for l in range(layers):
+            coli_moe_bank_fill(shape, host[l % host_layers], banks[l % 2], copy_stream=copy)
+
+    def compute_only():
+        for l in range(layers):
+            layer_compute(l)
+
+    def wall(fn, reps=2):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            h = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            el = time.perf_counter() - h
+            best = el if best is None else min(best, el)
+        return best
+
+    t_copy = wall(copies_only)
+    t_comp = wall(compute_only)
+    t_both = wall(streamed)
+    # one layer's compute (copy-bound) or one layer's copy (compute-bound) cannot overlap
+    ideal = max(t_copy + t_comp / layers, t_comp + t_copy / layers)
+    log(f"bank stream: copy {t_copy * 1e3:.1f} ms, compute {t_comp * 1e3:.2f} ms, streamed {t_both * 1e3:.1f} ms")
+    del banks, host, dev
+    torch.cuda.empty_cache()
+    return {"workload": f"stacked decode shape (T={T}), {layers} layers, every layer's routed experts "
+                        f"({layer_bytes / 1e9:.2f} GB bf16) streamed from pinned host memory through two device banks",
+            "copy_ms_per_layer": round(t_copy / layers * 1e3, 3),
+            "host_to_device_gbs": round(layer_bytes * layers / t_copy / 1e9, 1),
+            "compute_ms_per_layer": round(t_comp / layers * 1e3, 3),
+            "streamed_ms_per_layer": round(t_both / layers * 1e3, 3),
+            "tokens_per_s_streamed": round(T * layers / t_both, 1),
+            "overlap_efficiency": round(ideal / t_both, 4),
+            "note": "host clock around whole passes (best of 2); overlap_efficiency = ideal / streamed, ideal = "
+                    "max(copies + one layer's compute, computes + one layer's copy): 1 means everything that "
+                    "can overlap does"}
 
 
 # ---------------------------------------------------------------------------
@@ -415,6 +624,41 @@ def cpu_baseline(name, budget_s=15.0, tokens=None):
                       f"{E} experts, top-{K}, routed + shared FFN, in fp64 ({el:.1f} s)"}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_single_thread():
+    """The oracle on one core: the tiny fp32 layer (all 8 tokens) and the
+    first tokens of the decode batch."""
+    import oracle
+
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    out = {}
+    try:
+        for name, n in (("tiny", None), ("decode", 8)):
+            cfg, W = workload_inputs(name)
+            T, D, E, K, F = cfg["T"], cfg["D"], cfg["E"], cfg["K"], cfg["F"]
+            n = T if n is None else n
+            xs = W["x"][:n].copy()
+            t = time.perf_counter()
+            oracle.moe_layer(xs, W["wr"], W["bias"], W["gate"], W["up"], W["down"], W["s_gate"], W["s_up"],
+                             W["s_down"], n, D, E, K, F)
+            el = time.perf_counter() - t
+            out[name] = {"tokens_per_s": round(n / el, 3), "tokens": n, "seconds": round(el, 3)}
+    finally:
+        oracle.set_num_threads(threads)
+    return out
+
+
 def cpu_baseline_stacked(budget_s):
     """The oracle's chain over the 42 layers for the first n tokens (weights
     regenerated per layer; only the oracle's own time is counted)."""
@@ -450,6 +694,8 @@ def main():
                     help="override the workload's batch size T (not for stacked)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--quick", action="store_true",
+                    help="the named workload only (no decode, int4, stacked, dense, index or bank lines)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB device copy first (scale for counter runs)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
@@ -479,13 +725,27 @@ def main():
         main_res = run_stacked(args.steps, args.warmup, hip)
     else:
         main_res = run_workload(args.workload, args.steps, args.warmup, hip, args.tokens)
+    full = args.workload == "prefill" and args.tokens is None and not args.quick
     dec = None
-    if args.workload == "prefill" and not args.no_decode and args.tokens is None:
+    if args.workload == "prefill" and not args.no_decode and args.tokens is None and not args.quick:
         dec = run_workload("decode", args.steps, args.warmup, hip)
+    extra = {}
+    if full:
+        for nm in ("int4", "int4_decode"):
+            extra[nm] = layer_line(run_workload(nm, args.steps, args.warmup, hip))
+        extra["stacked"] = layer_line(run_stacked(max(2, args.steps // 5), 1, hip))
+        extra["dense"] = {nm: run_dense(nm, args.steps, args.warmup, hip)
+                          for nm in ("dense_decode", "dense_prefill")}
+        extra["index_topk"] = {nm: run_index_topk(nm, args.steps, args.warmup, hip)
+                               for nm in ("index_topk", "index_topk_decode")}
+        extra["bank_stream"] = run_bank_stream(hip)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(args.workload, tokens=args.tokens)
+        cpu["cpu_model"] = cpu_model()
+        if full:
+            cpu["single_thread"] = cpu_single_thread()
         log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} threads")
 
     cfg = main_res["cfg"]
@@ -500,6 +760,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(main_res["step_s"] * 1e3, 4),
+        "ms_per_step_median": round(main_res["step_median_s"] * 1e3, 4),
+        "ms_per_step_min": round(main_res["step_min_s"] * 1e3, 4),
+        "ms_per_step_instrumented": None if main_res.get("step_instrumented_s") is None
+        else round(main_res["step_instrumented_s"] * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -523,12 +787,27 @@ def main():
         "cpu_baseline": cpu,
     }
     if dec is not None:
-        out["decode"] = {"tokens_per_s": round(dec["tokens_per_s"], 1),
-                         "ms_per_step": round(dec["step_s"] * 1e3, 4),
-                         "hbm_gbs": dec["hbm_gbs"], "hbm_pct": dec["hbm_pct"],
-                         "nonempty_experts": dec["n_e"], "roofline": dec["roofline"],
-                         "stage_us": dec["stage_us"]}
+        out["decode"] = layer_line(dec)
+    out.update(extra)
     print(json.dumps(out), flush=True)
+
+
+def layer_line(r):
+    """The extra-workload entry of the JSON line for one MoE workload result."""
+    return {"workload": WORKLOAD_NAMES.get(r.get("name", ""), None) or
+                        f"T={r['cfg']['T']}, D={r['cfg']['D']}, F={r['cfg']['F']}, "
+                        f"{'int4 experts' if r['cfg'].get('int4') else r['cfg']['dtype']}"
+                        + (f", {r['cfg']['layers']} layers" if r['cfg'].get('layers', 1) > 1 else ""),
+            "tokens_per_s": round(r["tokens_per_s"], 1),
+            "ms_per_step": round(r["step_s"] * 1e3, 4),
+            "ms_per_step_median": round(r["step_median_s"] * 1e3, 4),
+            "ms_per_step_min": round(r["step_min_s"] * 1e3, 4),
+            "ms_per_step_instrumented": None if r.get("step_instrumented_s") is None
+            else round(r["step_instrumented_s"] * 1e3, 4),
+            "mfma_pct": r["mfma_pct"], "hbm_gbs": r["hbm_gbs"], "hbm_pct": r["hbm_pct"],
+            "nonempty_experts": r["n_e"],
+            "roofline": dict(r["roofline"], kernel="gate_up", avg_us=round(r["gu_s"] * 1e6, 2)),
+            "stage_us": r["stage_us"]}
 
 
 if __name__ == "__main__":

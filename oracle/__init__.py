@@ -92,12 +92,18 @@ def lib():
         L.oracle_index_topk.argtypes = [i64, i64, i64, vp, vp, i64, i64, vp]
         L.oracle_num_threads.restype = i32
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [i32]
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------

@@ -147,8 +147,10 @@ int oracle_dense_ffn(int64_t T, int64_t D, int64_t F, const orc_mat *x,
 int oracle_index_topk(int64_t rows, int64_t L, int64_t ld, const float *scores,
                       const int32_t *lens, int64_t k, int64_t tail, int32_t *idx);
 
-/* Threads the OpenMP loops use (1 when built without OpenMP). */
+/* Threads the OpenMP loops use (1 when built without OpenMP), and a way to
+ * change it (for timing the oracle on one core). */
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -37,11 +37,11 @@ coli_status check_shape(const coli_moe_shape *s)
 }
 
 struct RouteWs {
-    size_t z, tile_count, total;
+    size_t z, tile_count, done, total;
 };
 struct FfnWs {
     size_t h, o, sx, list_gu, list_dn, n_items, x16, total;
-    int bm;
+    int bm, ksplit;
 };
 
 RouteWs route_ws(const coli_moe_shape *s)
@@ -51,7 +51,8 @@ RouteWs route_ws(const coli_moe_shape *s)
     const size_t ntiles = (size_t)coli::perm_tiles(s->T);
     w.z = 0;
     w.tile_count = align_up(w.z + (size_t)coli::router_splits(s->T, s->D) * T * E * 4);
-    w.total = align_up(w.tile_count + ntiles * E * 4);
+    w.done = align_up(w.tile_count + ntiles * E * 4);
+    w.total = align_up(w.done + 4);
     return w;
 }
 
@@ -65,8 +66,9 @@ FfnWs ffn_ws(const coli_moe_shape *s, int quant)
     w.h = 0;
     w.o = align_up(w.h + (R + T) * F * elt);
     w.sx = align_up(w.o + R * D * elt);
+    w.ksplit = (s->dtype == COLI_BF16 && !quant) ? coli::ffn_down_splits(s->T, s->E, s->D, s->F, w.bm) : 1;
     const size_t max_tiles = (size_t)coli::ffn_max_tiles(s->T, s->E, s->K, w.bm);
-    w.list_gu = align_up(w.sx + T * D * 4);
+    w.list_gu = align_up(w.sx + T * D * 4 * (size_t)w.ksplit);
     w.list_dn = align_up(w.list_gu + max_tiles * (size_t)coli::ffn_col_tiles_gu(s->F) * 16);
     w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * 16);
     w.x16 = align_up(w.n_items + 20 * 4);
@@ -259,6 +261,7 @@ coli_status coli_moe_route_timed(const coli_moe_shape *s, const void *x, const v
     char *base = (char *)ws;
     a.z = (float *)(base + L.z);
     a.tile_count = (int32_t *)(base + L.tile_count);
+    a.done = (int32_t *)(base + L.done);
     a.ids = out->ids; a.w = out->w; a.count = out->count; a.offset = out->offset;
     a.perm = out->perm; a.inv = out->inv;
     coli::StageMarks marks{events, n_events, 0};
@@ -326,6 +329,7 @@ coli_status coli_moe_ffn_timed(const coli_moe_shape *s, const void *x, const col
     a.T = s->T; a.D = s->D; a.E = s->E; a.K = s->K; a.F = s->F;
     a.bf16 = s->dtype == COLI_BF16;
     a.bm = L.bm;
+    a.ksplit = L.ksplit;
     a.x = x;
     a.ids = r->ids; a.w = r->w; a.count = r->count; a.perm = r->perm;
     a.inv = r->inv;
@@ -382,6 +386,7 @@ coli_status coli_moe_ffn_int4_timed(const coli_moe_shape *s, const void *x,
     a.T = s->T; a.D = s->D; a.E = s->E; a.K = s->K; a.F = s->F;
     a.bf16 = true;
     a.bm = L.bm;
+    a.ksplit = L.ksplit;
     a.x = x;
     a.ids = r->ids; a.w = r->w; a.count = r->count; a.perm = r->perm;
     a.inv = r->inv;
@@ -438,6 +443,7 @@ coli_status coli_moe_dense_ffn(const coli_moe_shape *s, const void *x, const col
     a.T = s->T; a.D = s->D; a.E = 0; a.K = 0; a.F = s->F;
     a.bf16 = s->dtype == COLI_BF16;
     a.bm = L.bm;
+    a.ksplit = L.ksplit;
     a.x = x;
     a.s_gate = w->gate; a.s_up = w->up; a.s_down = w->down;
     a.residual = residual; a.y = y; a.y_bf16 = y_bf16;

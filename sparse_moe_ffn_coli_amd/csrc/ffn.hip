@@ -426,17 +426,23 @@ __global__ __launch_bounds__(256) void gateup_kernel(
 //    sx[t] = S_down h[R + t] in fp32 for the shared expert's rows.
 // ---------------------------------------------------------------------------
 
+// ksplit > 1 (layers without routed rows only): the reduction over F is cut
+// into ksplit equal parts, each a tile of its own, and part s of the shared
+// rows' output goes to sx + s * T * D; the combine adds the parts in order.
 template <class C>
 __global__ __launch_bounds__(256) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
-    const int32_t *__restrict__ count, int T, int D, int E, int K, int F,
+    const int32_t *__restrict__ count, int T, int D, int E, int K, int F, int ksplit,
     uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (D + C::BN - 1) / C::BN);
+    const int ncol = (D + C::BN - 1) / C::BN;
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, ncol * ksplit);
     if (et.e < 0) return;
     const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
-    const int d0 = et.ct * C::BN;                    // the last column tile may be ragged
+    const int sp = et.ct / ncol;                     // reduction part (0 unless split)
+    const int d0 = (et.ct - sp * ncol) * C::BN;      // the last column tile may be ragged
+    const int kl = F / ksplit, k0 = sp * kl;
     const int ch0 = threadIdx.x & 7;
 
     const uint16_t *ap[C::A_PER_T];
@@ -445,22 +451,22 @@ __global__ __launch_bounds__(256) void down_kernel(
     for (int i = 0; i < C::A_PER_T; ++i) {
         const int rr = a_chunk_row<C>(i);
         const int r = (rr < C::BM && et.m0 + rr < et.cnt) ? et.m0 + rr : et.m0;
-        ap[i] = h + (size_t)(et.base + r) * F + ch0 * 8;
+        ap[i] = h + (size_t)(et.base + r) * F + k0 + ch0 * 8;
     }
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i) {
         const int d = min(d0 + a_chunk_row<C>(i), D - 1);    // rows past D reread the last one
-        bp[i] = W + (size_t)d * F + ch0 * 8;
+        bp[i] = W + (size_t)d * F + k0 + ch0 * 8;
     }
     f32x16 acc[C::FM][C::FN];
-    mfma_mainloop<C>(ap, bp, F, lds, acc);
+    mfma_mainloop<C>(ap, bp, kl, lds, acc);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % C::WAVES_N, wm = wave / C::WAVES_N;
     const int dl = d0 + acc_col<C>(wn, 0, lane);
     const int r0 = wm * C::FM * 32 + 4 * (lane >> 5);
     if (et.shared)
-        frag_store_rows<C::FM, C::FN>(et, sx + dl, (size_t)D, 0, r0, D - dl,
+        frag_store_rows<C::FM, C::FN>(et, sx + (size_t)sp * T * D + dl, (size_t)D, 0, r0, D - dl,
                                       [&](int m, int n, int i) { return acc[m][n][i]; });
     else
         frag_store_rows<C::FM, C::FN>(et, o + dl, (size_t)D, et.base, r0, D - dl,
@@ -837,7 +843,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
 //    the routed rows); every routed row of the token is fetched before the
 //    fixed-order sum.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ sx, const uint16_t *__restrict__ o,
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ sx, int nsplit,
+                                                      const uint16_t *__restrict__ o,
                                                       const float *__restrict__ w, const int32_t *__restrict__ inv,
                                                       const float *residual, int T, int D, int K, float *y,
                                                       uint16_t *__restrict__ y_bf16)
@@ -854,6 +861,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sx + idx);
     const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sx + idx + 4);
     float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    for (int p = 1; p < nsplit; ++p) {            // parts of a split reduction, in order
+        const f32x4 q0 = *reinterpret_cast<const f32x4 *>(sx + (size_t)p * T * D + idx);
+        const f32x4 q1 = *reinterpret_cast<const f32x4 *>(sx + (size_t)p * T * D + idx + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] += q0[k];
+            v[4 + k] += q1[k];
+        }
+    }
     if (K > 0) {                                  // K = 0: a dense layer, no routed rows
         float wj[8];
         int iv[8];
@@ -987,6 +1003,19 @@ int ffn_tile_rows(int T, int E, int K, int int4)
     return int4 ? I4Cfg<64>::BM : BIG_BM;
 }
 
+// Parts of the down projection's reduction for a layer without routed rows
+// (E = 0) on the row-light tiles: enough tiles to occupy the GPU (up to 1024,
+// four workgroups per CU), each part a whole number of 64-wide steps.
+int ffn_down_splits(int T, int E, int D, int F, int bm)
+{
+    if (E != 0 || bm != SMALL_BM) return 1;
+    const long tiles = (long)((T + SMALL_BM - 1) / SMALL_BM) * ((D + SmallDownCfg::BN - 1) / SmallDownCfg::BN);
+    int best = 1;
+    for (int s = 2; s <= 16; ++s)
+        if ((F / 64) % s == 0 && tiles * s <= 1024) best = s;
+    return best;
+}
+
 long ffn_max_tiles(int T, int E, int K, int bm)
 {
     const long R = (long)T * K;
@@ -1001,7 +1030,8 @@ static void launch_combine(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     const long n = (long)a.T * (a.D / 8);
     mk.mark(st);
     combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-        a.sx, (const uint16_t *)a.o, a.w, a.inv, a.residual, a.T, a.D, a.K, a.y, (uint16_t *)a.y_bf16);
+        a.sx, max(a.ksplit, 1), (const uint16_t *)a.o, a.w, a.inv, a.residual, a.T, a.D, a.K, a.y,
+        (uint16_t *)a.y_bf16);
     mk.mark(st);
 }
 
@@ -1010,7 +1040,8 @@ static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
     const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
     const long grid_gu = xcd_grid(mt * ((a.F + C::BN / 2 - 1) / (C::BN / 2)));
-    const long grid_dn = xcd_grid(mt * ((a.D + CD::BN - 1) / CD::BN));
+    const int ks = max(a.ksplit, 1);
+    const long grid_dn = xcd_grid(mt * ((a.D + CD::BN - 1) / CD::BN) * ks);
     mk.mark(st);
     gateup_kernel<C><<<(unsigned)grid_gu, 256, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
@@ -1019,7 +1050,7 @@ static void launch_staged(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     mk.mark(st);
     down_kernel<CD><<<(unsigned)grid_dn, 256, 0, st>>>(
         (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.count,
-        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
+        a.T, a.D, a.E, a.K, a.F, ks, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 

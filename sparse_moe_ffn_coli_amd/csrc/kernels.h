@@ -27,6 +27,7 @@ struct RouteLaunch {
     const float *bias;
     float *z;              // workspace [router_splits][T][E]: partial logits
     int32_t *tile_count;   // workspace [perm_tiles(T)][E]
+    int32_t *done;         // workspace: counter of the fused top-K + permutation (zeroed by the router)
     int32_t *ids;
     float *w;
     int32_t *count, *offset, *perm, *inv;
@@ -52,7 +53,8 @@ struct FfnLaunch {
     void *h;               // workspace [T*K + T][F] (bf16; fp16 in the int4 engine's chunk order for int4)
     uint16_t *x16;         // workspace [T][D] (int4 only): x in fp16, the int4 engine's chunk order
     void *o;               // workspace [T*K][D]
-    float *sx;             // workspace [T][D] (bf16 path): the shared expert's output
+    float *sx;             // workspace [ksplit][T][D] (bf16 path): the shared expert's output (parts)
+    int ksplit;            // parts of the down reduction (layers without routed rows; else 1)
     int4 *list_gu;         // workspace [ffn_max_tiles * ffn_col_tiles_gu] (256-row tiles)
     int4 *list_dn;         // workspace [ffn_max_tiles * ffn_col_tiles_dn] (256-row tiles)
     int32_t *n_items;      // workspace [20]: list lengths and per-XCD range starts
@@ -70,5 +72,6 @@ int ffn_tile_rows(int T, int E, int K, int int4);
 long ffn_max_tiles(int T, int E, int K, int bm);
 int ffn_col_tiles_gu(int F);
 int ffn_col_tiles_dn(int D);
+int ffn_down_splits(int T, int E, int D, int F, int bm);
 
 }  // namespace coli

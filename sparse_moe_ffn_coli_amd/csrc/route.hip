@@ -39,8 +39,9 @@ constexpr int RT_MAX_SPLITS = 8;
 template <int NF>                    // 32-expert fragments per workgroup
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int D, int E, int splits,
-    float *__restrict__ zp)
+    float *__restrict__ zp, int32_t *__restrict__ done)
 {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *done = 0;     // the fused top-K's counter
     __shared__ float red[4 * NF * 16 * 64];         // [wave][frag][i][lane]
     const int n_nt = (E + 32 * NF - 1) / (32 * NF);
     const int n_mt = (T + RT_M - 1) / RT_M;
@@ -153,8 +154,9 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n)
 template <int NFW>                    // expert fragments per wave: nfrag <= 4 * NFW
 __global__ __launch_bounds__(512) void router_logits_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int D, int E, int splits,
-    int xs, int ws, float *__restrict__ zp)
+    int xs, int ws, float *__restrict__ zp, int32_t *__restrict__ done)
 {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *done = 0;     // the fused top-K's counter
     constexpr int CPW_MAX = 2 * NFW;              // router-row copies per wave per step
     __shared__ __attribute__((aligned(1024))) char lds[RL_LDS_BYTES];
     const int nfrag = (E + 31) / 32;
@@ -289,9 +291,10 @@ int router_splits(int T, int D)
 
 // fp32 router: one thread per (token, expert), plain dot product (one split).
 __global__ void router_logits_f32_kernel(const float *__restrict__ x, const float *__restrict__ wr, int T,
-                                         int D, int E, float *__restrict__ z)
+                                         int D, int E, float *__restrict__ z, int32_t *__restrict__ done)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) *done = 0;                        // the fused top-K's counter
     if (i >= (int64_t)T * E) return;
     int t = (int)(i / E), e = (int)(i % E);
     const float *xr = x + (size_t)t * D, *wrow = wr + (size_t)e * D;
@@ -326,16 +329,14 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o)
 
 constexpr int TOPK_MAX_E = 1024;
 
+// The top-K of token t by one wave; sel_e / sel_z: the wave's 8-entry LDS
+// scratch.
 template <int SLOTS, int NSP>          // NSP >= the number of reduction splits
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp, int splits,
-                                                   const float *__restrict__ bias, int T, int E, int K,
-                                                   int32_t *__restrict__ ids, float *__restrict__ w)
+__device__ __forceinline__ void topk_token(const float *__restrict__ zp, int splits, const float *__restrict__ bias,
+                                           int T, int E, int K, int t, int32_t *sel_e, float *sel_z,
+                                           int32_t *__restrict__ ids, float *__restrict__ w)
 {
-    __shared__ int32_t sel_e_s[4][8];
-    __shared__ float sel_z_s[4][8];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
-    if (t >= T) return;                           // whole waves: t is uniform in a wave
+    const int lane = threadIdx.x & 63;
 
     // logit = (split 0 + split 1 + ...) + bias; 0 marks an empty slot, every
     // real logit maps above 0 (NaN aside).  Every partial and bias of the
@@ -407,8 +408,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
     for (int s = 0; s < SLOTS; ++s) {
         if ((chosen[s] >> lane) & 1ull) {
             const int j = base + __popcll(chosen[s] & below);
-            sel_e_s[wave][j] = lane + 64 * s;
-            sel_z_s[wave][j] = from_ordered_bits(key[s]);
+            sel_e[j] = lane + 64 * s;
+            sel_z[j] = from_ordered_bits(key[s]);
         }
         base += __popcll(chosen[s]);
     }
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
     // cannot underflow the sum: sigmoid(a)/sigmoid(m) = e^(a-m) (1+e^m) / (1+e^a).
     // The maximum and the sum over lanes 0..7 are butterflies (every lane
     // ends with the same value, summed in the same order).
-    const float zl = (lane < K) ? sel_z_s[wave][lane] : -INFINITY;
+    const float zl = (lane < K) ? sel_z[lane] : -INFINITY;
     float zmax = zl;
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, o));
@@ -432,9 +433,22 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp,
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) psum += __shfl_xor(psum, o);
     if (lane < K) {
-        ids[(size_t)t * K + lane] = sel_e_s[wave][lane];
+        ids[(size_t)t * K + lane] = sel_e[lane];
         w[(size_t)t * K + lane] = pl / psum;
     }
+}
+
+template <int SLOTS, int NSP>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ zp, int splits,
+                                                   const float *__restrict__ bias, int T, int E, int K,
+                                                   int32_t *__restrict__ ids, float *__restrict__ w)
+{
+    __shared__ int32_t sel_e_s[4][8];
+    __shared__ float sel_z_s[4][8];
+    const int wave = threadIdx.x >> 6;
+    const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+    if (t >= T) return;                           // whole waves: t is uniform in a wave
+    topk_token<SLOTS, NSP>(zp, splits, bias, T, E, K, t, sel_e_s[wave], sel_z_s[wave], ids, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -568,11 +582,11 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
 constexpr int PERM_SMALL_T = 1024;
 constexpr int PERM_SMALL_MAX_E = 512;         // 16 waves x E masks of 8 bytes in LDS
 
-__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int E, int K,
-                                                          int32_t *__restrict__ count,
-                                                          int32_t *__restrict__ offset,
-                                                          int32_t *__restrict__ perm,
-                                                          int32_t *__restrict__ inv)
+// The small-batch permutation by one workgroup of 1024 threads (T <= 1024,
+// E <= 512); ids must be visible to the workgroup.
+__device__ __forceinline__ void perm_small_body(const int32_t *__restrict__ ids, int T, int E, int K,
+                                                int32_t *__restrict__ count, int32_t *__restrict__ offset,
+                                                int32_t *__restrict__ perm, int32_t *__restrict__ inv)
 {
     __shared__ uint64_t masks[16 * PERM_SMALL_MAX_E];
     __shared__ int32_t sc[1024];
@@ -613,6 +627,56 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
     }
 }
 
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int E, int K,
+                                                          int32_t *__restrict__ count,
+                                                          int32_t *__restrict__ offset,
+                                                          int32_t *__restrict__ perm,
+                                                          int32_t *__restrict__ inv)
+{
+    perm_small_body(ids, T, E, K, count, offset, perm, inv);
+}
+
+// ---------------------------------------------------------------------------
+// top-K and the small-batch permutation in one launch (T <= 1024, E <= 512):
+// workgroups of 16 waves, the first TOPK_PER_WG of which take one token each
+// (the top-K of a token is bound by instruction issue, so tokens are spread
+// over many CUs; the other waves are there for the permutation, which needs
+// all 16 in the one workgroup that runs it).  Each workgroup publishes its
+// ids (release fence, then a device-scope counter increment); the workgroup
+// that takes the counter to the grid size is the last one, and after an
+// acquire fence it sees every token's ids and builds the permutation.  The
+// counter is set to zero by the router kernel earlier on the same stream.
+// The permutation depends only on the ids, so it is the same whichever
+// workgroup is last.
+// ---------------------------------------------------------------------------
+constexpr int TOPK_PER_WG = 4;
+
+template <int SLOTS, int NSP>
+__global__ __launch_bounds__(1024) void topk_perm_kernel(const float *__restrict__ zp, int splits,
+                                                         const float *__restrict__ bias, int T, int E, int K,
+                                                         int32_t *__restrict__ ids, float *__restrict__ w,
+                                                         int32_t *__restrict__ done, int32_t *__restrict__ count,
+                                                         int32_t *__restrict__ offset, int32_t *__restrict__ perm,
+                                                         int32_t *__restrict__ inv)
+{
+    __shared__ int32_t sel_e_s[TOPK_PER_WG][8];
+    __shared__ float sel_z_s[TOPK_PER_WG][8];
+    __shared__ int32_t last_s;
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * TOPK_PER_WG + wave;
+    if (wave < TOPK_PER_WG && t < T)
+        topk_token<SLOTS, NSP>(zp, splits, bias, T, E, K, t, sel_e_s[wave], sel_z_s[wave], ids, w);
+    __syncthreads();                              // this workgroup's ids are written
+    if (threadIdx.x == 0) {
+        __threadfence();                          // release them device-wide
+        last_s = atomicAdd(done, 1) == (int)gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last_s) return;
+    __threadfence();                              // acquire: every workgroup's ids
+    perm_small_body(ids, T, E, K, count, offset, perm, inv);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -637,6 +701,19 @@ static void launch_topk(unsigned g, hipStream_t st, const float *z, int splits, 
     else topk_kernel<SLOTS, RT_MAX_SPLITS><<<g, 256, 0, st>>>(z, splits, bias, T, E, K, ids, w);
 }
 
+template <int SLOTS>
+static void launch_topk_perm(unsigned g, hipStream_t st, const RouteLaunch &a, int splits)
+{
+#define COLI_TOPK_PERM(NSP)                                                                               \
+    topk_perm_kernel<SLOTS, NSP><<<g, 1024, 0, st>>>(a.z, splits, a.bias, a.T, a.E, a.K, a.ids, a.w, a.done, \
+                                                     a.count, a.offset, a.perm, a.inv)
+    if (splits <= 1) COLI_TOPK_PERM(1);
+    else if (splits <= 2) COLI_TOPK_PERM(2);
+    else if (splits <= 4) COLI_TOPK_PERM(4);
+    else COLI_TOPK_PERM(RT_MAX_SPLITS);
+#undef COLI_TOPK_PERM
+}
+
 hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
 {
     const int T = a.T, D = a.D, E = a.E, K = a.K;
@@ -659,22 +736,35 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
             int xs = 0, ws = 0;
             router_lds_rings(E, &xs, &ws);
             const uint16_t *x = (const uint16_t *)a.x, *wr = (const uint16_t *)a.wr;
-            if (nfw == 1) router_logits_lds_kernel<1><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
-            else if (nfw == 2) router_logits_lds_kernel<2><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
-            else if (nfw == 3) router_logits_lds_kernel<3><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
-            else router_logits_lds_kernel<4><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z);
+            if (nfw == 1) router_logits_lds_kernel<1><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z, a.done);
+            else if (nfw == 2) router_logits_lds_kernel<2><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z, a.done);
+            else if (nfw == 3) router_logits_lds_kernel<3><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z, a.done);
+            else router_logits_lds_kernel<4><<<g, 512, 0, st>>>(x, wr, T, D, E, splits, xs, ws, a.z, a.done);
         } else if (T <= 512)
             router_logits_bf16_kernel<1><<<splits * n_mt * ((E + 31) / 32), 256, 0, st>>>(
-                (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z);
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z, a.done);
         else
             router_logits_bf16_kernel<2><<<splits * n_mt * ((E + 63) / 64), 256, 0, st>>>(
-                (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z);
+                (const uint16_t *)a.x, (const uint16_t *)a.wr, T, D, E, splits, a.z, a.done);
     } else {
         int64_t n = (int64_t)T * E;
         router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-            (const float *)a.x, (const float *)a.wr, T, D, E, a.z);
+            (const float *)a.x, (const float *)a.wr, T, D, E, a.z, a.done);
     }
     mk.mark(st);
+    if (T <= PERM_SMALL_T && E <= PERM_SMALL_MAX_E) {
+        // top-K and the permutation in one launch; the permutation stage is empty
+        const int g = (T + TOPK_PER_WG - 1) / TOPK_PER_WG, slots = (E + 63) / 64;
+        if (slots <= 1) launch_topk_perm<1>(g, st, a, splits);
+        else if (slots <= 2) launch_topk_perm<2>(g, st, a, splits);
+        else if (slots <= 3) launch_topk_perm<3>(g, st, a, splits);
+        else if (slots <= 4) launch_topk_perm<4>(g, st, a, splits);
+        else if (slots <= 5) launch_topk_perm<5>(g, st, a, splits);
+        else launch_topk_perm<8>(g, st, a, splits);
+        mk.mark(st);
+        mk.mark(st);
+        return hipGetLastError();
+    }
     {
         const int g = (T + 3) / 4, slots = (E + 63) / 64;
         if (slots <= 1) launch_topk<1>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
@@ -686,11 +776,6 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t st)
         else launch_topk<16>(g, st, a.z, splits, a.bias, T, E, K, a.ids, a.w);
     }
     mk.mark(st);
-    if (T <= PERM_SMALL_T && E <= PERM_SMALL_MAX_E) {
-        perm_small_kernel<<<1, 1024, 0, st>>>(a.ids, T, E, K, a.count, a.offset, a.perm, a.inv);
-        mk.mark(st);
-        return hipGetLastError();
-    }
     const int ntiles = perm_tiles(T);
     perm_hist_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_count);
     perm_scatter_kernel<<<ntiles, PERM_TILE, 0, st>>>(a.ids, T, E, K, a.tile_count, ntiles, a.count, a.offset,
