@@ -47,6 +47,26 @@ SMALL = [
 ]
 
 
+# small batches at reduction widths of 512, 1024 and 2048: experts with several
+# row tiles, a shared expert whose last tile is ragged, K = 4, int4 experts with
+# groups of 32 and 64
+SMALL_BATCH = [
+    # cid, T, D, E, K, F, int4, group
+    (140, 50, 512, 40, 8, 192, False, 32),
+    (141, 37, 1024, 64, 8, 128, True, 32),
+    (142, 131, 2048, 288, 8, 256, False, 32),
+    (143, 71, 2048, 96, 8, 64, True, 64),
+    (144, 9, 512, 16, 4, 64, True, 32),
+]
+
+
+@pytest.mark.parametrize("cid,T,D,E,K,F,int4,group", SMALL_BATCH)
+def test_small_batches(cid, T, D, E, K, F, int4, group):
+    cfg = custom_cfg(cid, T, D, E, K, F, "bf16", int4=int4, group=group)
+    W = make_inputs(cfg)
+    _report(f"small batch cid={cid} int4={int4}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label=f"cid={cid}"))
+
+
 @pytest.mark.parametrize("cid,T,D,E,K,F,dt,bias", SMALL)
 def test_small_shapes(cid, T, D, E, K, F, dt, bias):
     cfg = custom_cfg(cid, T, D, E, K, F, dt, bias=bias)
