@@ -50,6 +50,10 @@ WORKLOAD_NAMES = {
 }
 
 
+# workloads around the MoE layer, measured on their own with --workload
+EXTRA_WORKLOADS = ("dense_decode", "dense_prefill", "index_topk", "index_topk_decode")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -689,7 +693,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", default="prefill",
+                    choices=sorted(WORKLOAD_NAMES) + sorted(EXTRA_WORKLOADS))
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's batch size T (not for stacked)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -718,6 +723,20 @@ def main():
     if args.copy_calibration:
         copy_calibration()
 
+    if args.workload in EXTRA_WORKLOADS:
+        if args.workload.startswith("dense"):
+            r = run_dense(args.workload, args.steps, args.warmup, hip)
+            line = {"metric": f"dense FFN tokens/s ({args.workload})", "value": r["tokens_per_s"],
+                    "unit": "tokens/s", "ms_per_step": round(r["us_per_layer"] / 1e3, 5), "dtype": "bf16"}
+        else:
+            r = run_index_topk(args.workload, args.steps, args.warmup, hip)
+            line = {"metric": f"index top-k rows/s ({args.workload})", "value": r["rows_per_s"],
+                    "unit": "rows/s", "ms_per_step": round(r["us_per_call"] / 1e3, 5), "dtype": "f32"}
+        line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                     "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded generator, seed 0)",
+                     "config": {"workload": r["workload"]}, "roofline": r["roofline"], "detail": r})
+        print(json.dumps(line), flush=True)
+        return
     if args.tokens is not None and (args.workload == "stacked" or args.tokens < 1):
         print("--tokens takes a positive batch size and a single-layer workload", file=sys.stderr)
         sys.exit(2)
