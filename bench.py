@@ -68,7 +68,7 @@ def log(msg):
 # only while the sources still hash the same.
 # ---------------------------------------------------------------------------
 KERNEL_SOURCES = ("sparse_moe_ffn_coli_amd/csrc/ffn.hip", "sparse_moe_ffn_coli_amd/csrc/route.hip",
-                  "sparse_moe_ffn_coli_amd/csrc/device_common.h")
+                  "sparse_moe_ffn_coli_amd/csrc/select.hip", "sparse_moe_ffn_coli_amd/csrc/device_common.h")
 COPY_BYTES = 256 << 20
 
 
