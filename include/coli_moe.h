@@ -22,10 +22,12 @@
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller (the expert
  *     bank fill also takes pinned HOST pointers, stated there).  The library
- *     never allocates, frees or synchronises.  Its only process-wide state
- *     is a per-device cache of the device-architecture check (each entry set
- *     once to a fixed answer).  Scratch memory is the caller's workspace
- *     (`ws`, `ws_bytes`), sized by the matching *_workspace_bytes() call.
+ *     never allocates, frees or synchronises.  Its process-wide state is a
+ *     per-device cache of the device-architecture check (each entry set once
+ *     to a fixed answer) and, for coli_moe_ffn_noalloc only, a per-device
+ *     scratch array and its address.  Scratch memory is otherwise the
+ *     caller's workspace (`ws`, `ws_bytes`), sized by the matching
+ *     *_workspace_bytes() call.
  *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
  *     stream).  All work is enqueued on it in order; calls return before the
  *     GPU finishes.
@@ -182,7 +184,10 @@ coli_status coli_moe_ffn_int4(const coli_moe_shape *s, const void *x,
  * `stream`: events[i] just before stage i is enqueued and events[n_stages]
  * after the last one.  Entries past n_events, and NULL entries, are skipped.
  * Nothing is recorded when the call fails validation or T = 0.
- *   route stages (3): router logits, top-K, permutation
+ *   route stages (3): router logits, top-K, permutation (for T <= 1024 and
+ *                     E <= 512 top-K and the permutation are one kernel,
+ *                     timed as the top-K stage; the permutation stage is
+ *                     then empty)
  *   ffn stages (3):   gate+up (+SwiGLU), down (routed and shared), combine;
  *                     a preparation kernel (the tile lists for large batches,
  *                     the x -> fp16 pass for int4) runs before events[0], so

@@ -329,6 +329,19 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o)
 
 constexpr int TOPK_MAX_E = 1024;
 
+// Maximum over the 64 lanes of a wave (all lanes active), returned in every
+// lane: pairs, quads, half rows and rows by DPP, then the four row maxima.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
 // The top-K of token t by one wave; sel_e / sel_z: the wave's 8-entry LDS
 // scratch.
 template <int SLOTS, int NSP>          // NSP >= the number of reduction splits
@@ -371,33 +384,33 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ zp, int spl
 #pragma unroll
         for (int sp = 1; sp < NSP; ++sp)
             if (sp < splits) v += part[s][sp];
-        key[s] = (lane + 64 * s < E) ? ordered_bits(v + bs[s]) : 0u;
+        // real experts map to images >= 1 (only a NaN could map to 0), so a
+        // padding slot (image 0) is never among the K taken below
+        key[s] = (lane + 64 * s < E) ? max(ordered_bits(v + bs[s]), 1u) : 0u;
     }
-    // tau: the K-th largest image
-    uint32_t tau = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s) cnt += __popcll(__ballot(key[s] >= cand));
-        if (cnt >= K) tau = cand;
-    }
-    // chosen: all images above tau, then images equal to tau by ascending index
+    // the K largest images one per round: the wave maximum m of the images
+    // not yet taken, then the lowest expert index holding m (slots, then
+    // lanes, ascending) is taken.  Equal images therefore go to the lower
+    // index, and the K taken are the first K of the order (image desc, index asc).
     uint64_t chosen[SLOTS];
-    int need = K;
+    uint32_t rem[SLOTS];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-        chosen[s] = __ballot(key[s] > tau);
-        need -= __popcll(chosen[s]);
-    }
+    for (int s = 0; s < SLOTS; ++s) { chosen[s] = 0ull; rem[s] = key[s]; }
+    for (int j = 0; j < K; ++j) {
+        uint32_t m = rem[0];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-        uint64_t eq = __ballot(key[s] == tau);
-        while (need > 0 && eq) {
-            const uint64_t low = eq & (~eq + 1);   // lowest set bit
-            chosen[s] |= low;
-            eq ^= low;
-            --need;
+        for (int s = 1; s < SLOTS; ++s) m = max(m, rem[s]);
+        m = wave_max_u32(m);
+        bool taken = false;
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const uint64_t b = __ballot(rem[s] == m);
+            if (!taken && b) {
+                const uint64_t low = b & (~b + 1);   // lowest set bit
+                chosen[s] |= low;
+                if ((low >> lane) & 1ull) rem[s] = 0u;
+                taken = true;
+            }
         }
     }
     // output position of each chosen expert: chosen experts of lower slots,
@@ -592,7 +605,8 @@ __device__ __forceinline__ void perm_small_body(const int32_t *__restrict__ ids,
     __shared__ int32_t sc[1024];
     __shared__ int32_t ws[16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
+    const int nw = (T + 63) >> 6;                 // waves that hold tokens
+    for (int i = tid; i < nw * E; i += 1024) masks[i] = 0ull;
     __syncthreads();
     int ev[8];
     if (tid < T) {
@@ -604,7 +618,7 @@ __device__ __forceinline__ void perm_small_body(const int32_t *__restrict__ ids,
     __syncthreads();
     int c = 0;
     if (tid < E)
-        for (int w2 = 0; w2 < 16; ++w2) c += __popcll(masks[w2 * E + tid]);
+        for (int w2 = 0; w2 < nw; ++w2) c += __popcll(masks[w2 * E + tid]);
     sc[tid] = block_scan_incl_1024(c, ws);
     __syncthreads();
     if (tid < E) {
