@@ -837,4 +837,167 @@ __device__ __forceinline__ void i4_mainloop(const uint16_t *const (&arow)[C::ARO
     }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow form of the int4 engine for tiles that hold few token rows
+// (decode-sized batches).  An int4 pass multiplies 8 token rows: the A
+// fragment rows repeat them (fragment row r reads token row r mod 8), so
+// rows 0-7 of the results are the pass's rows and the rest are dropped; a
+// tile with more real rows takes several passes over its weights.  The small
+// A stage leaves LDS for stages of 256 reduction elements, i.e. whole
+// 128-byte lines of every weight row per stage (a streaming probe of this
+// tile's copies measured 5.9 TB/s with 128-byte pieces of 256 rows per
+// stage against 4.7 TB/s with the 64-byte pieces of the staged engine).  The
+// scales never pass through LDS: lane l of wave w holds the 64 scales of
+// weight row 64 w + l in registers, which are exactly the rows of its wave's
+// two B fragments, and v_permlane32_swap hands each lane the words of its
+// fragments' rows (an LDS store after LDS-DMA copies would also make the
+// compiler wait for every copy in flight).  bf16 tiles (the shared expert)
+// keep all 32 rows with 64-element stages of the same size.  Scales must
+// fill at most one 128-byte line per weight row (group 32, K a multiple of
+// 256 and at most 2048: i4n_fits).
+// LDS: B [256 rows][128 B], A int4 [4 blocks of 64][8 rows][128 B], A bf16
+// [32 rows][128 B]; chunk c of row r sits in slot c ^ (r & 7).
+// ---------------------------------------------------------------------------
+struct I4NCfg {
+    static constexpr int BM = 32, BN = 256, NT = 256;
+    static constexpr int WAVES_M = 1, WAVES_N = 4, FM = 1, FN = 2;
+    static constexpr int KS_I4 = 256, KS_BF = 64;    // reduction elements per stage
+    static constexpr int AR = 8;                      // token rows of an int4 pass
+    static constexpr int B_BYTES = BN * 128;
+    static constexpr int A_BYTES = 4096;              // 8 rows x 256 fp16, or 32 rows x 64 bf16
+    static constexpr int STAGE_BYTES = B_BYTES + A_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int WAVES_PER_EU = 2;
+};
+static_assert(I4NCfg::LDS_BYTES * 2 <= 160 * 1024, "two workgroups per CU");
+
+// Whether the narrow engine can take a product of reduction width K: the
+// scales of a row in one line, the reduction in whole stages.
+__host__ __device__ inline bool i4n_fits(int K, int group)
+{
+    return group == 32 && K % 256 == 0 && K / 32 <= 64;
+}
+
+// fp16 bits in half h of a 32-bit word, in both halves of the result
+__device__ __forceinline__ f16x2 half_splat(uint32_t word, int h)
+{
+    const uint32_t b = (word >> (16 * h)) & 0xffffu;
+    return __builtin_bit_cast(f16x2, b * 0x00010001u);
+}
+
+// One pass of a tile.  brow[j]: weight row 64 w + 8 j + lane / 8 (byte 0).
+// I4: ap = token row lane / 8 of the pass (element 0, fp16 in chunk order),
+// srow = the scales of weight row tid.  bf16: a0 + r * lda = token row r
+// (r < valid), srow unused.
+template <bool I4>
+__device__ __forceinline__ void i4n_mainloop(const uint16_t *ap, const uint16_t *a0, int lda,
+                                             const char *const (&brow)[8], const uint16_t *srow, int K, int valid,
+                                             char *lds, f32x16 (&acc)[I4NCfg::FN])
+{
+    using C = I4NCfg;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;
+    constexpr int KS = I4 ? C::KS_I4 : C::KS_BF;
+    const int nk = K / KS;
+    auto dma = [](const void *src, char *dst) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    };
+    u32x4 sv[8];                                      // scales of weight row tid: sv[i] = stage i's eight
+    if (I4) {
+        const int n16 = K / 256;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sv[i] = *reinterpret_cast<const u32x4 *>(srow + 8 * min(i, n16 - 1));
+    }
+    const int cr = lane >> 3, cp = lane & 7;          // a copy's row within its 8 and its slot
+    const int ab = min(w * 8 + cr, valid - 1);        // bf16: this lane's A row
+    auto issue = [&](int kt) {
+        char *sb = lds + (kt & 1) * C::STAGE_BYTES, *sa = sb + C::B_BYTES;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {                 // B: 8 rows of 128 bytes per copy
+            const int c = cp ^ cr;                    // rows 64 w + 8 j + cr: (row & 7) = cr
+            if (I4) dma(brow[j] + kt * 128 + c * 16, sb + (w * 8 + j) * 1024);
+            else dma(brow[j] + (kt * KS + c * 8) * 2, sb + (w * 8 + j) * 1024);
+        }
+        if (I4) dma(ap + kt * KS + w * 64 + (cp ^ cr) * 8, sa + w * 1024);        // block w, rows 0-7
+        else dma(a0 + (size_t)ab * lda + kt * KS + (cp ^ cr) * 8, sa + w * 1024);  // rows 8 w .. 8 w + 7
+    };
+
+#pragma unroll
+    for (int n = 0; n < C::FN; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
+    const int ar = lane & 31;                         // A fragment row
+    const int arn = ar & 7;                           // its pass row (int4)
+    int br[C::FN];                                    // B fragment rows: 64 w + 32 n + lane % 32
+#pragma unroll
+    for (int n = 0; n < C::FN; ++n) br[n] = (w * C::FN + n) * 32 + (lane & 31);
+
+    issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt_c<0>();                            // stage kt has landed
+        // LDS-only barrier: every wave's copies of stage kt are visible, and
+        // every wave is done with stage kt - 1, whose slot the next issue
+        // overwrites
+        __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < nk) issue(kt + 1);
+        const char *sb = lds + (kt & 1) * C::STAGE_BYTES, *sa = sb + C::B_BYTES;
+        if (I4) {
+            // stage kt's scales of rows 64 w + lane % 32 (n = 0) and
+            // 64 w + 32 + lane % 32 (n = 1), from lanes lane % 32 and
+            // 32 + lane % 32: word q holds groups 2 q (low) and 2 q + 1
+            const u32x4 own = sv[0];
+#pragma unroll
+            for (int i = 0; i < 7; ++i) sv[i] = sv[i + 1];
+            uint32_t sword[C::FN][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const auto x = __builtin_amdgcn_permlane32_swap(own[q], own[q], false, false);
+                sword[0][q] = x[0];
+                sword[1][q] = x[1];
+            }
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const int c = 2 * blk + h;            // 16-byte chunk = scale group 2 blk + h
+                u32x4 bq[C::FN];
+                f16x2 sc[C::FN];
+#pragma unroll
+                for (int n = 0; n < C::FN; ++n) {
+                    bq[n] = *reinterpret_cast<const u32x4 *>(sb + br[n] * 128 + ((c ^ (br[n] & 7)) * 16));
+                    sc[n] = half_splat(sword[n][blk], h);
+                }
+                f16x8 a[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int ca = 4 * h + j;
+                    a[j] = *reinterpret_cast<const f16x8 *>(sa + (blk * 8 + arn) * 128 + ((ca ^ arn) * 16));
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int n = 0; n < C::FN; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            a[j], __builtin_bit_cast(f16x8, int4x8_to_f16x8(bq[n][j], sc[n])), acc[n], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 2 * j + h;
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sa + ar * 128 + ((c ^ (ar & 7)) * 16));
+#pragma unroll
+                for (int n = 0; n < C::FN; ++n) {
+                    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(sb + br[n] * 128 + ((c ^ (br[n] & 7)) * 16));
+                    acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[n], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // the slots are reused by the next pass or tile: every wave is done
+    // reading them
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+}
+
 }  // namespace coli

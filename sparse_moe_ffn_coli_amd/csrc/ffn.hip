@@ -835,6 +835,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PE
                                   [&](int, int n, int i) { return f32_to_bf16_bits(acc[n][i]); });
 }
 
+// The gate+up product on the narrow engine (few rows per expert tile): the
+// tiles and outputs are those of gateup_int4_kernel; an int4 tile runs one
+// pass per 8 of its real rows, and each pass stores its own rows.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(I4NCfg::WAVES_PER_EU))) void gateup_int4n_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ x16, const uint8_t *__restrict__ gate_q, const uint16_t *__restrict__ gate_s,
+    const uint8_t *__restrict__ up_q, const uint16_t *__restrict__ up_s,
+    const uint16_t *__restrict__ s_gate, const uint16_t *__restrict__ s_up,
+    const int32_t *__restrict__ count, const int32_t *__restrict__ perm, int T, int D, int E, int K, int F,
+    uint16_t *__restrict__ h16)
+{
+    using C = I4NCfg;
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
+    constexpr int FC = C::BN / 2;
+    const ExpertTile et = find_tile(count, E, T, T * K, C::BM, (F + TILE_N / 2 - 1) / (TILE_N / 2));
+    if (et.e < 0) return;
+    const int f0 = et.ct * FC;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int valid = min(et.cnt - et.m0, C::BM);
+
+    // weight row tr of the tile: block tr / 32 holds gate (even) or up (odd)
+    // rows f0 + (block / 2) * 32 ..; rows past F read row F - 1
+    auto wrow = [&](int tr) { return min(f0 + ((tr >> 5) >> 1) * 32 + (tr & 31), F - 1); };
+    const char *brow[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int tr = w * 64 + j * 8 + (lane >> 3);
+        const bool upb = (tr >> 5) & 1;
+        brow[j] = et.shared
+            ? reinterpret_cast<const char *>((upb ? s_up : s_gate) + (size_t)wrow(tr) * D)
+            : reinterpret_cast<const char *>((upb ? up_q : gate_q) + ((size_t)et.e * F + wrow(tr)) * (D / 2));
+    }
+    const int fo = f0 + w * (C::FN / 2) * 32 + (lane & 31);
+    const int r0 = 4 * (lane >> 5);
+    f32x16 acc[C::FN];
+    if (et.shared) {
+        i4n_mainloop<false>(nullptr, x + (size_t)et.m0 * D, D, brow, nullptr, D, valid, lds, acc);
+        frag_store_rows<1, C::FN / 2>(et, h16 + fo, (size_t)F, et.base, r0, F - fo, [&](int, int p, int i) {
+            return f32_to_bf16_bits(swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
+        });
+        return;
+    }
+    const int tr = threadIdx.x;
+    const uint16_t *srow = (((tr >> 5) & 1) ? up_s : gate_s) + ((size_t)et.e * F + wrow(tr)) * (D / 32);
+    const int fs = (fo & ~7) + f16_chunk_slot(fo & 7);
+    for (int p0 = 0; p0 < valid; p0 += C::AR) {
+        int r = et.m0 + p0 + (lane >> 3);             // this lane's A row of the pass
+        if (r >= et.cnt) r = et.m0 + p0;
+        const uint16_t *ap = x16 + (size_t)(perm[et.base + r] / K) * D;
+        i4n_mainloop<true>(ap, nullptr, 0, brow, srow, D, valid, lds, acc);
+        ExpertTile ep = et;
+        ep.m0 = et.m0 + p0;
+        ep.cnt = min(et.cnt, ep.m0 + C::AR);
+        frag_store_rows<1, C::FN / 2>(ep, h16 + fs, (size_t)F, et.base, r0, F - fo, [&](int, int p, int i) {
+            return __builtin_bit_cast(uint16_t, (_Float16)swiglu_clamped_fast(acc[2 * p][i], acc[2 * p + 1][i]));
+        });
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 3. combine: per token t and column d,
 //      v = sx[t][d]; v = fmaf(w_tj, o[inv(t,j)][d], v) for j = 0..K-1;
@@ -987,6 +1045,7 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 using SmallGuCfg = TileCfg<32, 128, 1, 4>;
 using SmallDownCfg = TileCfg<32, 128, 1, 4>;
 constexpr int SMALL_BM = SmallGuCfg::BM;
+constexpr int I4N_MAX_T = 128;    // int4 batches up to this size run the narrow engine
 constexpr int BIG_BM = BigCfg::BM;
 static_assert(SmallDownCfg::BM == SMALL_BM && I4Cfg<32>::BM == SMALL_BM, "row-light paths share the tile height");
 static_assert(I4Cfg<64>::BN == TILE_N && I4Cfg<32>::BN == TILE_N && BigCfg::BN == TILE_N,
@@ -1093,6 +1152,29 @@ static void launch_staged_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t s
     launch_combine(a, mk, st);
 }
 
+static void launch_narrow_int4(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
+{
+    using C = I4NCfg;
+    static_assert(C::BM == I4Cfg<32>::BM, "the narrow gate+up and the staged down share the tiles");
+    const long mt = ffn_max_tiles(a.T, a.E, a.K, C::BM);
+    const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
+    const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
+    const long n8 = (long)a.T * a.D / 8;
+    x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint16_t *)a.x, n8, a.x16);
+    mk.mark(st);                                     // the gate+up stage is its kernel alone
+    gateup_int4n_kernel<<<(unsigned)grid_gu, 256, 0, st>>>(
+        (const uint16_t *)a.x, a.x16, a.gate_q, a.gate_s, a.up_q, a.up_s,
+        (const uint16_t *)a.s_gate, (const uint16_t *)a.s_up, a.count, a.perm,
+        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.h);
+    mk.mark(st);
+    // the down product stays on the staged engine (same tiles, same h16
+    // layout), which was measured as fast or faster for these batches
+    down_int4_kernel<I4Cfg<32>><<<(unsigned)grid_dn, 256, 0, st>>>(
+        (const uint16_t *)a.h, a.down_q, a.down_s, a.group, (const uint16_t *)a.s_down, a.count,
+        a.T, a.D, a.E, a.K, a.F, (uint16_t *)a.o, a.sx);
+    launch_combine(a, mk, st);
+}
+
 hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
 {
     const int T = a.T, D = a.D, K = a.K, F = a.F;
@@ -1101,7 +1183,9 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
     StageMarks &mk = a.marks ? *a.marks : none;
     if (a.bf16) {
         if (a.use_int4) {
-            if (a.bm == SMALL_BM)
+            if (a.bm == SMALL_BM && a.T <= I4N_MAX_T && i4n_fits(a.D, a.group))
+                launch_narrow_int4(a, mk, st);
+            else if (a.bm == SMALL_BM)
                 launch_staged_int4<I4Cfg<32>>(a, mk, st);
             else
                 launch_staged_int4<I4Cfg<64>>(a, mk, st);

@@ -141,21 +141,40 @@ def test_int4_stacked_layer_shape_every_token():
             compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4 T=256"))
 
 
-def test_int4_small_scales():
+# batches of at most 128 tokens with group-32 scales and D a multiple of 256
+# run the gate+up product on the narrow int4 engine: 8 token rows per pass, so
+# experts with more rows take several passes over one tile (150: about 50 rows
+# per expert; 151: D = 256, a single stage; 152: a single token; 153: the
+# largest batch that takes this engine; 154: small scales; the small shapes
+# 131, 134, 141 and 144 above take it too)
+@pytest.mark.parametrize("cid,T,D,E,K,F", [
+    (150, 100, 512, 16, 8, 256),
+    (151, 64, 256, 288, 8, 256),
+    (152, 1, 2048, 288, 8, 768),
+    (153, 128, 1024, 64, 8, 512),
+])
+def test_int4_narrow_engine(cid, T, D, E, K, F):
+    cfg = custom_cfg(cid, T, D, E, K, F, "bf16", int4=True, group=32)
+    W = make_inputs(cfg)
+    _report(f"int4 narrow cid={cid}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label=f"int4 narrow cid={cid}"))
+
+
+@pytest.mark.parametrize("cid,F", [(134, 128), (154, 256)])
+def test_int4_small_scales(cid, F):
     # group scales in [2^-14, 2^-12), where a scale divided by 16 would be an fp16
     # subnormal: each weight must still be (nibble - 8) * scale rounded once.  The
     # tokens are scaled by 128 (exact in bf16) so the products keep their size, and
     # the shared expert is zero so that y is the routed experts' output alone.
-    cfg = custom_cfg(134, 90, 256, 24, 8, 128, "bf16", int4=True, group=32)
+    cfg = custom_cfg(cid, 90, 256, 24, 8, F, "bf16", int4=True, group=32)
     W = make_inputs(cfg)
-    rng = np.random.default_rng(134)
+    rng = np.random.default_rng(cid)
     for k in ("gate_s", "up_s", "down_s"):
         W[k] = rng.integers(0x0400, 0x0C00, size=W[k].shape, dtype=np.uint16)
     for k in ("s_gate", "s_up", "s_down"):
         W[k] = np.zeros_like(W[k])
     x32 = (W["x"].astype(np.uint32) << 16).view(np.float32) * np.float32(128.0)
     W["x"] = (x32.view(np.uint32) >> 16).astype(np.uint16)
-    _report("int4 small scales", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4 small scales"))
+    _report(f"int4 small scales F={F}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label="int4 small scales"))
 
 
 # ---------------------------------------------------------------------------
