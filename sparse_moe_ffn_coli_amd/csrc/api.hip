@@ -70,7 +70,8 @@ FfnWs ffn_ws(const coli_moe_shape *s, int quant)
     const size_t max_tiles = (size_t)coli::ffn_max_tiles(s->T, s->E, s->K, w.bm);
     w.list_gu = align_up(w.sx + T * D * 4 * (size_t)w.ksplit);
     w.list_dn = align_up(w.list_gu + max_tiles * (size_t)coli::ffn_col_tiles_gu(s->F) * 16);
-    w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * 16);
+    // the down list holds every column tile once per part of the reduction
+    w.n_items = align_up(w.list_dn + max_tiles * (size_t)coli::ffn_col_tiles_dn(s->D) * (size_t)w.ksplit * 16);
     w.x16 = align_up(w.n_items + 20 * 4);
     w.total = quant ? align_up(w.x16 + T * D * 2) : w.x16;
     return w;

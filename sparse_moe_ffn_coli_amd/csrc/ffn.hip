@@ -602,24 +602,27 @@ __device__ __forceinline__ void gateup_big_tile(
 
 template <int NFW>
 __device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg::CPW], const ExpertTile &et,
-                                              int d0, int D, int F, int w, char *lds,
+                                              int d0, int D, int kl, int w, char *lds,
                                               uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     f32x16 acc[BigCfg::FM][BigCfg::FN];
-    big_mainloop<BigCfg, NFW>(rp, F, min(et.cnt - et.m0, BigCfg::BM), w, lds, acc);
+    big_mainloop<BigCfg, NFW>(rp, kl, min(et.cnt - et.m0, BigCfg::BM), w, lds, acc);
     const int lane = threadIdx.x & 63, wn = w & 1;
     const int dl = d0 + wn * BigCfg::FN * 32 + (lane & 31);   // column of fragment n: dl + 32 n
     if (et.shared) big_store_rows<NFW>(acc, et, sx + dl, (size_t)D, 0, D - dl, w, [](float v) { return v; });
     else big_store_rows<NFW>(acc, et, o + dl, (size_t)D, et.base, D - dl, w, [](float v) { return f32_to_bf16_bits(v); });
 }
 
+// k0, kl: the part of the reduction over F this tile covers (all of it but
+// for layers without routed rows, whose parts write their own slices of sx).
 __device__ __forceinline__ void down_big_tile(
     const ExpertTile &et, const uint16_t *__restrict__ h, const uint16_t *__restrict__ down,
-    const uint16_t *__restrict__ s_down, int D, int F, char *lds, uint16_t *__restrict__ o,
+    const uint16_t *__restrict__ s_down, int D, int F, int k0, int kl, char *lds, uint16_t *__restrict__ o,
     float *__restrict__ sx)
 {
     const int d0 = et.ct * BigCfg::BN;
-    const uint16_t *W = et.shared ? s_down : down + (size_t)et.e * D * F;
+    const uint16_t *W = (et.shared ? s_down : down + (size_t)et.e * D * F) + k0;
+    h += k0;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (et.cnt - et.m0 <= StreamCfg::A_ROWS) {
         using S = StreamRows;
@@ -633,7 +636,7 @@ __device__ __forceinline__ void down_big_tile(
             rb[j] = W + (size_t)min(d0 + br, D - 1) * F + big_copy_chunk<S>(br) * 8;
         }
         f32x16 acc[4];
-        stream_mainloop(ra, rb, F, et.cnt - et.m0, w, lds, acc);
+        stream_mainloop(ra, rb, kl, et.cnt - et.m0, w, lds, acc);
         if ((w >> 2) != 0) return;
         const int dl = d0 + (w & 1) * 128 + (threadIdx.x & 31);
         if (et.shared)
@@ -656,9 +659,9 @@ __device__ __forceinline__ void down_big_tile(
         rp[BigCfg::CPO + j] = W + (size_t)d * F + ch * 8;
     }
     const int nfw = big_wave_fragments(et.cnt - et.m0, w >> 1);
-    if (nfw == 2) down_big_body<2>(rp, et, d0, D, F, w, lds, o, sx);
-    else if (nfw == 1) down_big_body<1>(rp, et, d0, D, F, w, lds, o, sx);
-    else down_big_body<0>(rp, et, d0, D, F, w, lds, o, sx);
+    if (nfw == 2) down_big_body<2>(rp, et, d0, D, kl, w, lds, o, sx);
+    else if (nfw == 1) down_big_body<1>(rp, et, d0, D, kl, w, lds, o, sx);
+    else down_big_body<0>(rp, et, d0, D, kl, w, lds, o, sx);
 }
 
 // Between two tiles of a workgroup: every wave has finished reading LDS
@@ -688,16 +691,23 @@ __global__ __launch_bounds__(512) void gateup_big_kernel(
     }
 }
 
+// ksplit > 1 (layers without routed rows only): the list's column tiles run
+// over ncol * ksplit, tile c covering columns (c % ncol) and part c / ncol of
+// the reduction, whose sums go to slice c / ncol of sx.
 __global__ __launch_bounds__(512) void down_big_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ down, const uint16_t *__restrict__ s_down,
-    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int D, int E, int F,
+    const int4 *__restrict__ list, const int32_t *__restrict__ n_items, int T, int D, int E, int F, int ksplit,
     uint16_t *__restrict__ o, float *__restrict__ sx)
 {
     __shared__ __attribute__((aligned(1024))) char lds[BIG_LDS_BYTES];
     const int xc = blockIdx.x & 7;
     const int beg = max(n_items[11 + xc], 0), end = min(n_items[11 + xc + 1], n_items[0]);
+    const int ncol = (D + BigCfg::BN - 1) / BigCfg::BN, kl = F / ksplit;
     for (int t = beg + (blockIdx.x >> 3); t < end; t += gridDim.x >> 3) {
-        down_big_tile(list_tile(list[t], E), h, down, s_down, D, F, lds, o, sx);
+        ExpertTile et = list_tile(list[t], E);
+        const int sp = et.ct / ncol;
+        et.ct -= sp * ncol;
+        down_big_tile(et, h, down, s_down, D, F, sp * kl, kl, lds, o, sx + (size_t)sp * T * D);
         tile_barrier();
     }
 }
@@ -1063,15 +1073,28 @@ int ffn_tile_rows(int T, int E, int K, int int4)
 }
 
 // Parts of the down projection's reduction for a layer without routed rows
-// (E = 0) on the row-light tiles: enough tiles to occupy the GPU (up to 1024,
-// four workgroups per CU), each part a whole number of 64-wide steps.
+// (E = 0), each part a whole number of 64-wide steps.  Row-light tiles:
+// enough tiles to occupy the GPU (up to 1024, four workgroups per CU).
+// 256 x 256 tiles (one workgroup per CU): the fewest parts that give every
+// CU a tile, since each part adds a T x D slice of fp32 partial sums (at
+// most 8; the most parts below that when no count reaches every CU).
 int ffn_down_splits(int T, int E, int D, int F, int bm)
 {
-    if (E != 0 || bm != SMALL_BM) return 1;
-    const long tiles = (long)((T + SMALL_BM - 1) / SMALL_BM) * ((D + SmallDownCfg::BN - 1) / SmallDownCfg::BN);
+    if (E != 0) return 1;
+    if (bm == SMALL_BM) {
+        const long tiles = (long)((T + SMALL_BM - 1) / SMALL_BM) * ((D + SmallDownCfg::BN - 1) / SmallDownCfg::BN);
+        int best = 1;
+        for (int s = 2; s <= 16; ++s)
+            if ((F / 64) % s == 0 && tiles * s <= 1024) best = s;
+        return best;
+    }
+    const long tiles = (long)((T + BIG_BM - 1) / BIG_BM) * ((D + TILE_N - 1) / TILE_N);
     int best = 1;
-    for (int s = 2; s <= 16; ++s)
-        if ((F / 64) % s == 0 && tiles * s <= 1024) best = s;
+    for (int s = 1; s <= 8; ++s)
+        if ((F / 64) % s == 0) {
+            best = s;
+            if (tiles * s >= 256) break;
+        }
     return best;
 }
 
@@ -1117,9 +1140,10 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
 {
     const long mt = ffn_max_tiles(a.T, a.E, a.K, BigCfg::BM);
     const long grid_gu = xcd_grid(mt * ffn_col_tiles_gu(a.F));
-    const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D));
+    const int ks = max(a.ksplit, 1);
+    const long grid_dn = xcd_grid(mt * ffn_col_tiles_dn(a.D) * ks);
     ffn_tiles_kernel<<<2, 1024, 0, st>>>(a.count, a.E, a.T, a.T * a.K, ffn_col_tiles_gu(a.F),
-                                         ffn_col_tiles_dn(a.D), a.list_gu, a.list_dn, a.n_items);
+                                         ffn_col_tiles_dn(a.D) * ks, a.list_gu, a.list_dn, a.n_items);
     mk.mark(st);                                     // the gate+up stage is its kernel alone
     gateup_big_kernel<<<(unsigned)grid_gu, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.x, (const uint16_t *)a.gate, (const uint16_t *)a.up,
@@ -1128,7 +1152,7 @@ static void launch_big(const FfnLaunch &a, StageMarks &mk, hipStream_t st)
     mk.mark(st);
     down_big_kernel<<<(unsigned)grid_dn, BigCfg::NT, 0, st>>>(
         (const uint16_t *)a.h, (const uint16_t *)a.down, (const uint16_t *)a.s_down, a.list_dn,
-        a.n_items, a.D, a.E, a.F, (uint16_t *)a.o, a.sx);
+        a.n_items, a.T, a.D, a.E, a.F, ks, (uint16_t *)a.o, a.sx);
     launch_combine(a, mk, st);
 }
 

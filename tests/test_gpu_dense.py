@@ -44,9 +44,10 @@ def _inputs(cid, T, D, F, dtype):
 
 @pytest.mark.parametrize("cid,T,D,F,dtype", [
     (201, 40, 128, 192, "bf16"),      # 32-row tiles, a ragged last row tile
-    (202, 600, 256, 320, "bf16"),     # 256-row tiles (T >= 512), ragged rows and columns
+    (202, 600, 256, 320, "bf16"),     # 256-row tiles (T >= 512), ragged rows and columns, 5 down parts
     (203, 1, 64, 64, "bf16"),         # one token, minimum widths
     (204, 30, 128, 64, "f32"),
+    (205, 1024, 2048, 512, "bf16"),   # 256-row tiles, the down reduction in 8 parts
 ])
 def test_dense_small_shapes(cid, T, D, F, dtype):
     W = _inputs(cid, T, D, F, dtype)
