@@ -159,6 +159,21 @@ def test_int4_narrow_engine(cid, T, D, E, K, F):
     _report(f"int4 narrow cid={cid}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label=f"int4 narrow cid={cid}"))
 
 
+# bf16 routed batches on the row-light tiles (R <= 24 E): 160 about 21 rows per
+# expert, 161 a single token at the workload widths, 162 K = 4, 163 128 tokens
+# over 288 experts
+@pytest.mark.parametrize("cid,T,D,E,K,F", [
+    (160, 128, 256, 48, 8, 256),
+    (161, 1, 2048, 288, 8, 768),
+    (162, 90, 512, 64, 4, 384),
+    (163, 128, 1024, 288, 8, 512),
+])
+def test_bf16_row_light_batches(cid, T, D, E, K, F):
+    cfg = custom_cfg(cid, T, D, E, K, F, "bf16")
+    W = make_inputs(cfg)
+    _report(f"bf16 row-light cid={cid}", compare(run_gpu(W, cfg), run_oracle(W, cfg), cfg, label=f"cid={cid}"))
+
+
 @pytest.mark.parametrize("cid,F", [(134, 128), (154, 256)])
 def test_int4_small_scales(cid, F):
     # group scales in [2^-14, 2^-12), where a scale divided by 16 would be an fp16
@@ -194,6 +209,9 @@ def test_int4_small_scales(cid, F):
     # (6 slots run as 8, 10 as 16): every slot's loads stay inside the logits and bias
     (118, 40, 64, 330, 8, 64, "bf16"),
     (119, 40, 64, 600, 8, 64, "bf16"),
+    # fp32 above the fused top-K + permutation path: the fp32 router zeroes the
+    # per-tile counts that the top-K kernel accumulates
+    (120, 1100, 64, 40, 8, 64, "f32"),
 ])
 def test_edge_shapes(cid, T, D, E, K, F, dt):
     cfg = custom_cfg(cid, T, D, E, K, F, dt)
