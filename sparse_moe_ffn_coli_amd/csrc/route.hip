@@ -306,12 +306,10 @@ __global__ void router_logits_f32_kernel(const float *__restrict__ x, const floa
 // ---------------------------------------------------------------------------
 // top-K: one wave per token.  Lane l holds the logits of experts l, l+64, ...
 // (slot s: expert 64 s + l) as order-preserving unsigned images of the fp32
-// values.  The K-th largest image tau is found bit by bit, most significant
-// first: a candidate bit stays set when at least K images are >= the
-// candidate (counted with one ballot per slot), so after 32 steps tau is
-// the K-th largest value.  The chosen experts are every image above tau and,
-// of those equal to tau, the lowest expert indices until K are taken (ties go
-// to the lower index).  Since the index is 64 s + l, slot-major lane order is
+// values.  K rounds each take the largest remaining image (a DPP wave
+// maximum) at its lowest expert index (ballots over the slots in order), so
+// the K taken are the first K of the order (image desc, index asc): ties go
+// to the lower index.  Since the index is 64 s + l, slot-major lane order is
 // ascending index order, so each chosen expert's output position is a
 // prefix popcount of the chosen masks: the ids come out ascending.
 // ---------------------------------------------------------------------------
