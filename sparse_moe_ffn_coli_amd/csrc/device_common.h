@@ -360,9 +360,80 @@ __device__ __forceinline__ void big_wait_stages(int pending)
     }
 }
 
+// One step of a full tile (every A row real, both fragments of every wave
+// used) with a two-stage ring, in a fixed instruction order.  The wave reads
+// the step's first fragments, then runs its four MFMA groups, reading the
+// fragments of group kk + 1 while group kk runs (one LDS read after each of
+// the first six MFMAs).  Its eight copies of stage kt + 1 go out one after
+// each MFMA of group SLOT: waves 0-3 in group 0, waves 4-7 (the second wave
+// of each SIMD) in group 2.  A copy instruction moves 1 KB and the CU's
+// address path takes about 16 cycles for it, so a wave that issues copies
+// stalls until they are accepted; with all eight waves issuing at the start
+// of the step, every SIMD's matrix core waited for both of its waves (a
+// timestamped build measured the second wave of each SIMD held 44 % of the
+// loop), while staggered, one wave of each SIMD multiplies while the other is
+// held.  sched_barrier(0) after every MFMA keeps this order.
+template <class C, bool MORE, int SLOT>
+__device__ __forceinline__ void big_full_step(const uint16_t *const (&rp)[C::CPW], int kt, int w, char *lds,
+                                              f32x16 (&acc)[C::FM][C::FN], bf16x8 (&af)[2][C::FM],
+                                              bf16x8 (&bfr)[2][C::FN])
+{
+    static_assert(C::NS == 2 && C::FM == 2 && C::FN == 4 && C::CPW == C::FM * C::FN, "step shape");
+    constexpr int KK = C::BK / 16;
+    const int lane = threadIdx.x & 63;
+    const int wm = w >> 1, wn = w & 1;
+    const char *st = lds + (kt & 1) * C::STAGE_BYTES;
+    char *nst = lds + ((kt + 1) & 1) * C::STAGE_BYTES;
+    // fragment f of group kk (0, 1: A rows of fragment m = f; 2..5: B rows of fragment n = f - 2)
+    auto frag = [&](int kk, int f) -> bf16x8 {
+        const int c = kk * 2 + (lane >> 5);
+        const int r = (f < 2) ? (wm * C::FM + f) * 32 + (lane & 31) : (wn * C::FN + f - 2) * 32 + (lane & 31);
+        const char *base = (f < 2) ? st : st + C::OPERAND_BYTES;
+        return *reinterpret_cast<const bf16x8 *>(base + (r * C::CPR + big_swz_pos<C>(r, c)) * 16);
+    };
+    wait_vmcnt_c<0>();
+    asm volatile("s_barrier" ::: "memory");            // see big_mainloop
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        if (f < 2) af[0][f] = frag(0, f);
+        else bfr[0][f - 2] = frag(0, f);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const int slot = kk & 1;
+#pragma unroll
+        for (int i = 0; i < C::FM * C::FN; ++i) {
+            const int m = i / C::FN, n = i % C::FN;
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][m], bfr[slot][n], acc[m][n], 0, 0, 0);
+            if (kk + 1 < KK && i < 6) {
+                if (i < 2) af[slot ^ 1][i] = frag(kk + 1, i);
+                else bfr[slot ^ 1][i - 2] = frag(kk + 1, i);
+            }
+            if (MORE && kk == SLOT) {                   // copy i of stage kt + 1 (i < CPO: A rows, else B)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(rp[i] + (kt + 1) * C::BK),
+                    (__attribute__((address_space(3))) void *)(nst + (i / C::CPO) * C::OPERAND_BYTES +
+                                                               ((i % C::CPO) * 8 + w) * 1024),
+                    16, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <class C, int SLOT>
+__device__ __forceinline__ void big_full_loop(const uint16_t *const (&rp)[C::CPW], int nk, int w, char *lds,
+                                              f32x16 (&acc)[C::FM][C::FN])
+{
+    bf16x8 af[2][C::FM], bfr[2][C::FN];
+    for (int kt = 0; kt + 1 < nk; ++kt) big_full_step<C, true, SLOT>(rp, kt, w, lds, acc, af, bfr);
+    if (nk > 0) big_full_step<C, false, SLOT>(rp, nk - 1, w, lds, acc, af, bfr);
+}
+
 // rp[j]: this lane's source for copy j at k = 0 (row big_copy_row(j, w),
 // chunk big_copy_chunk(row) already applied; j < CPO: A, else B), readable
-// for every k < K.  w = this wave (0..7), wm = w >> 1, wn = w & 1.
+// for every k < K.  w = this wave (0..7), wm = w >> 1, wn = w & 1.  Full
+// tiles (valid = BM) take big_full_loop.
 template <class C, int NFW>
 __device__ __forceinline__ void big_mainloop(const uint16_t *const (&rp)[C::CPW], int K, int valid, int w,
                                              char *lds, f32x16 (&acc)[C::FM][C::FN])
@@ -409,6 +480,13 @@ __device__ __forceinline__ void big_mainloop(const uint16_t *const (&rp)[C::CPW]
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
         if (s < nk) COLI_BIG_ISSUE(s);
+    if constexpr (C::NS == 2 && NFW == 2) {
+        if (valid >= C::BM) {                          // a full tile: every copy is issued, every wave has NFW = 2
+            if (w < 4) big_full_loop<C, 0>(rp, nk, w, lds, acc);
+            else big_full_loop<C, 2>(rp, nk, w, lds, acc);
+            return;
+        }
+    }
     if constexpr (C::NS >= 3) {
         // With three or more stages the barrier of step kt comes before its
         // last MFMA group and also covers stage kt + 1 (issued two steps
