@@ -365,20 +365,26 @@ __device__ __forceinline__ void big_wait_stages(int pending)
 // the step's first fragments, then runs its four MFMA groups, reading the
 // fragments of group kk + 1 while group kk runs (one LDS read after each of
 // the first six MFMAs).  Its eight copies of stage kt + 1 go out one after
-// each MFMA of group SLOT: waves 0-3 in group 0, waves 4-7 (the second wave
-// of each SIMD) in group 2.  A copy instruction moves 1 KB and the CU's
-// address path takes about 16 cycles for it, so a wave that issues copies
-// stalls until they are accepted; with all eight waves issuing at the start
-// of the step, every SIMD's matrix core waited for both of its waves (a
-// timestamped build measured the second wave of each SIMD held 44 % of the
-// loop), while staggered, one wave of each SIMD multiplies while the other is
-// held.  sched_barrier(0) after every MFMA keeps this order.
-template <class C, bool MORE, int SLOT>
+// each of MFMAs BASE, BASE + STRIDE, ... of the step: waves 0-3 after MFMAs
+// 0..7 (group 0), waves 4-7 (the second wave of each SIMD) after MFMAs 8..15
+// (group 1).  A copy instruction moves 1 KB and the CU's address path takes
+// about 16 cycles for it, so a wave that issues copies stalls until they are
+// accepted; with all eight waves issuing at the start of the step, every
+// SIMD's matrix core waited for both of its waves (a timestamped build
+// measured the second wave of each SIMD held 44 % of the loop), while
+// staggered, one wave of each SIMD multiplies while the other is held.  The
+// second wave's copies go out one group later, not two: with two, they were
+// still in flight when the next step began (HBM latency is about 1 us) --
+// group 1 against group 2 measured 0.62 against 0.63 ms for the prefill step
+// and 0.38-0.39 against 0.40 ms for the dense one.  sched_barrier(0) after
+// every MFMA keeps this order.
+template <class C, bool MORE, int BASE, int STRIDE>
 __device__ __forceinline__ void big_full_step(const uint16_t *const (&rp)[C::CPW], int kt, int w, char *lds,
                                               f32x16 (&acc)[C::FM][C::FN], bf16x8 (&af)[2][C::FM],
                                               bf16x8 (&bfr)[2][C::FN])
 {
     static_assert(C::NS == 2 && C::FM == 2 && C::FN == 4 && C::CPW == C::FM * C::FN, "step shape");
+    static_assert(BASE + (C::CPW - 1) * STRIDE < (C::BK / 16) * C::FM * C::FN, "copies inside the step");
     constexpr int KK = C::BK / 16;
     const int lane = threadIdx.x & 63;
     const int wm = w >> 1, wn = w & 1;
@@ -409,11 +415,13 @@ __device__ __forceinline__ void big_full_step(const uint16_t *const (&rp)[C::CPW
                 if (i < 2) af[slot ^ 1][i] = frag(kk + 1, i);
                 else bfr[slot ^ 1][i - 2] = frag(kk + 1, i);
             }
-            if (MORE && kk == SLOT) {                   // copy i of stage kt + 1 (i < CPO: A rows, else B)
+            const int g = kk * C::FM * C::FN + i;        // MFMA index within the step
+            if (MORE && g >= BASE && (g - BASE) % STRIDE == 0 && (g - BASE) / STRIDE < C::CPW) {
+                const int j = (g - BASE) / STRIDE;        // copy j of stage kt + 1 (j < CPO: A rows, else B)
                 __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(rp[i] + (kt + 1) * C::BK),
-                    (__attribute__((address_space(3))) void *)(nst + (i / C::CPO) * C::OPERAND_BYTES +
-                                                               ((i % C::CPO) * 8 + w) * 1024),
+                    (const __attribute__((address_space(1))) void *)(rp[j] + (kt + 1) * C::BK),
+                    (__attribute__((address_space(3))) void *)(nst + (j / C::CPO) * C::OPERAND_BYTES +
+                                                               ((j % C::CPO) * 8 + w) * 1024),
                     16, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -421,13 +429,13 @@ __device__ __forceinline__ void big_full_step(const uint16_t *const (&rp)[C::CPW
     }
 }
 
-template <class C, int SLOT>
+template <class C, int BASE, int STRIDE>
 __device__ __forceinline__ void big_full_loop(const uint16_t *const (&rp)[C::CPW], int nk, int w, char *lds,
                                               f32x16 (&acc)[C::FM][C::FN])
 {
     bf16x8 af[2][C::FM], bfr[2][C::FN];
-    for (int kt = 0; kt + 1 < nk; ++kt) big_full_step<C, true, SLOT>(rp, kt, w, lds, acc, af, bfr);
-    if (nk > 0) big_full_step<C, false, SLOT>(rp, nk - 1, w, lds, acc, af, bfr);
+    for (int kt = 0; kt + 1 < nk; ++kt) big_full_step<C, true, BASE, STRIDE>(rp, kt, w, lds, acc, af, bfr);
+    if (nk > 0) big_full_step<C, false, BASE, STRIDE>(rp, nk - 1, w, lds, acc, af, bfr);
 }
 
 // rp[j]: this lane's source for copy j at k = 0 (row big_copy_row(j, w),
@@ -482,8 +490,8 @@ __device__ __forceinline__ void big_mainloop(const uint16_t *const (&rp)[C::CPW]
         if (s < nk) COLI_BIG_ISSUE(s);
     if constexpr (C::NS == 2 && NFW == 2) {
         if (valid >= C::BM) {                          // a full tile: every copy is issued, every wave has NFW = 2
-            if (w < 4) big_full_loop<C, 0>(rp, nk, w, lds, acc);
-            else big_full_loop<C, 2>(rp, nk, w, lds, acc);
+            if (w < 4) big_full_loop<C, 0, 1>(rp, nk, w, lds, acc);        // copies after MFMAs 0..7
+            else big_full_loop<C, C::FM * C::FN, 1>(rp, nk, w, lds, acc);  // after MFMAs 8..15
             return;
         }
     }
