@@ -569,7 +569,10 @@ __device__ __forceinline__ void big_mainloop(const uint16_t *const (&rp)[C::CPW]
 // rows), four for B rows as in big_mainloop.  The waves of the first two
 // rows (w < 4) multiply, one 32-row fragment each (A rows 32 (w / 2) ..,
 // skipped when that fragment has no real row), against B fragments
-// 4 (w % 2) .. + 3.
+// 4 (w % 2) .. + 3; they issue their copies after their MFMAs, so the
+// copy-issue queue (about 16 cycles per 1 KB copy instruction on a CU) never
+// holds their matrix work, and the three-stage lead leaves the copies two
+// steps to land (prefill gate+up 353 -> 348 us).
 // ---------------------------------------------------------------------------
 struct StreamCfg {
     static constexpr int BK = 64, NS = 4, A_ROWS = 64;
@@ -633,7 +636,7 @@ __device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16
     for (int kt = 0; kt < nk; ++kt) {
         stream_wait(min(C::NS - 2, nk - 1 - kt), cw);     // stages after kt still in flight
         asm volatile("s_barrier" ::: "memory");               // see big_mainloop
-        if (kt + C::NS - 1 < nk) COLI_ST_ISSUE(kt + C::NS - 1);
+        if (kt + C::NS - 1 < nk && w >= 4) COLI_ST_ISSUE(kt + C::NS - 1);
         if (mma) {
             const char *st = lds + (kt % C::NS) * C::STAGE_BYTES;
 #pragma unroll
@@ -651,6 +654,7 @@ __device__ __forceinline__ void stream_mainloop(const uint16_t *ra, const uint16
                     acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[n], acc[n], 0, 0, 0);
             }
         }
+        if (w < 4 && kt + C::NS - 1 < nk) COLI_ST_ISSUE(kt + C::NS - 1);   // after the MFMAs: see above
     }
 #undef COLI_ST_ISSUE
 }

@@ -491,17 +491,18 @@ __device__ __forceinline__ int big_wave_fragments(int rows, int wm)
 // column 32 n of the lane's column `out` points at; each real row's pointer
 // is formed once and its FN values stored at immediate offsets.  out_row0:
 // the output row of the tile's first row minus et.m0; cols: columns left
-// from the lane's first (fragments at or past it are dropped).
+// from the lane's first (fragments at or past it are dropped); full: every
+// row and column of the tile real (the same for all lanes, so the wave takes
+// one branch).
 template <int NFW, class T, class Cvt>
 __device__ __forceinline__ void big_store_rows(const f32x16 (&acc)[BigCfg::FM][BigCfg::FN], const ExpertTile &et,
-                                               T *out, size_t ld, int out_row0, int cols, int w, Cvt cvt)
+                                               T *out, size_t ld, int out_row0, int cols, bool full, int w, Cvt cvt)
 {
     const int lane = threadIdx.x & 63, wm = w >> 1;
     const int rows = et.cnt - et.m0;
     const int r0 = wm * 64 + 4 * (lane >> 5);
     T *const base = out + (size_t)(out_row0 + et.m0) * ld;
-    if (rows >= BigCfg::BM && __builtin_amdgcn_readfirstlane(cols) >= 32 * BigCfg::FN && cols >= 32 * BigCfg::FN) {
-        // every row and column real (a full tile): no checks
+    if (full) {                                   // no checks
 #pragma unroll
         for (int m = 0; m < NFW; ++m)
 #pragma unroll
@@ -609,8 +610,10 @@ __device__ __forceinline__ void down_big_body(const uint16_t *const (&rp)[BigCfg
     big_mainloop<BigCfg, NFW>(rp, kl, min(et.cnt - et.m0, BigCfg::BM), w, lds, acc);
     const int lane = threadIdx.x & 63, wn = w & 1;
     const int dl = d0 + wn * BigCfg::FN * 32 + (lane & 31);   // column of fragment n: dl + 32 n
-    if (et.shared) big_store_rows<NFW>(acc, et, sx + dl, (size_t)D, 0, D - dl, w, [](float v) { return v; });
-    else big_store_rows<NFW>(acc, et, o + dl, (size_t)D, et.base, D - dl, w, [](float v) { return f32_to_bf16_bits(v); });
+    const bool full = et.cnt - et.m0 >= BigCfg::BM && d0 + BigCfg::BN <= D;
+    if (et.shared) big_store_rows<NFW>(acc, et, sx + dl, (size_t)D, 0, D - dl, full, w, [](float v) { return v; });
+    else big_store_rows<NFW>(acc, et, o + dl, (size_t)D, et.base, D - dl, full, w,
+                             [](float v) { return f32_to_bf16_bits(v); });
 }
 
 // k0, kl: the part of the reduction over F this tile covers (all of it but
