@@ -180,9 +180,10 @@ __device__ __forceinline__ ExpertTile find_tile(const int32_t *__restrict__ coun
 // gate+up list, [2..10] gate+up range starts (x = 0..8), [11..19] down.
 constexpr int TILE_COST0 = 208;
 
-// Sets starts[0..8]: entry q goes to XCD floor(8 * (cost of entries before q) / total).
+// Sets starts[0..8] (in LDS): entry q goes to XCD floor(8 * (cost of entries
+// before q) / total).
 template <class Cost>
-__device__ __forceinline__ void xcd_split(int n, Cost &&cost, int32_t *__restrict__ starts)
+__device__ __forceinline__ void xcd_split(int n, Cost &&cost, int32_t *starts)
 {
     __shared__ int32_t csum[1024];
     __shared__ int32_t ws[16];
@@ -228,11 +229,20 @@ __device__ __forceinline__ void xcd_split(int n, Cost &&cost, int32_t *__restric
 // Two workgroups, one per list (both phases are bound by instruction issue on
 // one CU, so the lists are built side by side).  Each reads the counts once;
 // the owner of every row tile goes into an LDS table, so each list entry is
-// computed once, from LDS alone, together with its cost, which stays in LDS
-// for the split.  Lists longer than the LDS tables recompute entries by
-// binary search.
+// computed from LDS alone, once for its cost, which stays in LDS for the
+// split, and once more when it is written to its place after the split.
+// Lists longer than the LDS tables recompute entries by binary search and
+// keep list order.
 constexpr int TILES_LDS_ROWS = 4096;     // row tiles with an owner entry in LDS
 constexpr int TILES_LDS_COST = 8192;     // entries per list with a cost in LDS
+// The last TAIL_Q entries of every XCD range (about 1.5 per CU) are placed
+// in decreasing cost (ties in list order): an XCD's CUs take its range in
+// order as they free up, so the range ends on its cheapest tiles instead of
+// whichever full tiles the expert order put last (prefill gate+up 339 ->
+// 326 us).  Only the tail is sorted: in list order the CUs of an XCD run
+// weight-streaming (few-row) and MFMA-bound (full) tiles side by side,
+// which keeps both HBM and the matrix cores busy.
+constexpr int TAIL_Q = 48;
 
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restrict__ count, int E, int T,
                                                          int R, int nnt_gu, int nnt_dn,
@@ -293,15 +303,37 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t *__restri
     const int nnt = gu ? nnt_gu : nnt_dn;
     int4 *__restrict__ list = gu ? list_gu : list_dn;
     const int n = (routed + mt_sh) * nnt;
+    // lists whose costs all fit in LDS are written after the split, with
+    // their range tails sorted; longer ones are written in list order
+    const bool sort_tails = n <= TILES_LDS_COST;
     for (int q = tid; q < n; q += 1024) {
         const int4 en = entry(q, nnt);
-        list[q] = en;
+        if (!sort_tails) list[q] = en;
         if (q < TILES_LDS_COST) cost_s[q] = (int16_t)cost_of(en);
     }
     if (tid == 0) n_items[gu ? 1 : 0] = n;
     __syncthreads();
-    xcd_split(n, [&](int q) { return q < TILES_LDS_COST ? (int)cost_s[q] : cost_of(entry(q, nnt)); },
-              n_items + (gu ? 2 : 2 + 9));
+    __shared__ int32_t starts[9];
+    xcd_split(n, [&](int q) { return q < TILES_LDS_COST ? (int)cost_s[q] : cost_of(entry(q, nnt)); }, starts);
+    if (tid < 9) n_items[(gu ? 2 : 2 + 9) + tid] = starts[tid];
+    if (!sort_tails) return;
+    for (int q = tid; q < n; q += 1024) {
+        int x = 0;                                // range of q: starts[x] <= q < starts[x + 1]
+#pragma unroll
+        for (int xx = 1; xx < 8; ++xx) x += (q >= starts[xx]) ? 1 : 0;
+        const int s1 = starts[x + 1], s0 = max(starts[x], s1 - TAIL_Q);
+        int pos = q;
+        if (q >= s0) {                            // rank in the tail: costlier entries, then earlier equal ones
+            const int c = cost_s[q];
+            int rank = 0;
+            for (int j = s0; j < s1; ++j) {
+                const int cj = cost_s[j];
+                rank += (cj > c || (cj == c && j < q)) ? 1 : 0;
+            }
+            pos = s0 + rank;
+        }
+        list[pos] = entry(q, nnt);
+    }
 }
 
 // List entry of the 256 x 256 kernels: {e | ct << 16, m0, cnt, base}.
