@@ -639,6 +639,80 @@ __device__ __forceinline__ void perm_small_body(const int32_t *__restrict__ ids,
     }
 }
 
+// The same stable counting sort for a batch of at most 64 tokens, by one
+// wave with no barriers (lane t holds token t): masks[e] gets bit t when
+// token t chose expert e, lane l counts and scans experts l * epl .. + epl
+// - 1 (epl = ceil(E / 64)), and a token's rank among an expert's tokens is
+// the popcount of the mask below its bit.  Wave-scope fences order the LDS
+// phases (the lanes of one wave run in lockstep, but the compiler must not
+// move a lane's reads of other lanes' words across them).  ids must be
+// visible to the wave.
+constexpr int PERM_WAVE_T = 64;
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void perm_wave_body(const int32_t *__restrict__ ids, int T, int E, int K,
+                                               int32_t *__restrict__ count, int32_t *__restrict__ offset,
+                                               int32_t *__restrict__ perm, int32_t *__restrict__ inv)
+{
+    __shared__ uint64_t wmask[PERM_SMALL_MAX_E];
+    __shared__ int32_t wfirst[PERM_SMALL_MAX_E];
+    const int lane = threadIdx.x & 63;
+    const int epl = (E + 63) >> 6;                // at most 8 (E <= 512)
+    for (int e = lane; e < E; e += 64) wmask[e] = 0ull;
+    int ev[8];
+    if (lane < T) load_token_ids(ids, lane, K, ev);
+    wave_lds_sync();
+    if (lane < T) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K) atomicOr((unsigned long long *)&wmask[ev[j]], 1ull << lane);
+    }
+    wave_lds_sync();
+    int c[8], tot = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = lane * epl + i;
+        c[i] = (i < epl && e < E) ? __popcll(wmask[e]) : 0;
+        tot += c[i];
+    }
+    int inc = tot;                                // inclusive scan of the lanes' totals
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(inc, off);
+        if (lane >= off) inc += u;
+    }
+    int run = inc - tot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = lane * epl + i;
+        if (i < epl && e < E) {
+            count[e] = c[i];
+            offset[e] = run;
+            wfirst[e] = run;
+            run += c[i];
+        }
+    }
+    if (lane == 63) offset[E] = inc;
+    wave_lds_sync();
+    if (lane < T) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j >= K) break;
+            const int e = ev[j];
+            const int row = wfirst[e] + __popcll(wmask[e] & below);
+            perm[row] = lane * K + j;
+            inv[(size_t)lane * K + j] = row;
+        }
+    }
+}
+
 __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int E, int K,
                                                           int32_t *__restrict__ count,
                                                           int32_t *__restrict__ offset,
@@ -653,13 +727,17 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
 // workgroups of 16 waves, the first TOPK_PER_WG of which take one token each
 // (the top-K of a token is bound by instruction issue, so tokens are spread
 // over many CUs; the other waves are there for the permutation, which needs
-// all 16 in the one workgroup that runs it).  Each workgroup publishes its
-// ids (release fence, then a device-scope counter increment); the workgroup
-// that takes the counter to the grid size is the last one, and after an
-// acquire fence it sees every token's ids and builds the permutation.  The
-// counter is set to zero by the router kernel earlier on the same stream.
-// The permutation depends only on the ids, so it is the same whichever
-// workgroup is last.
+// all 16 in the one workgroup that runs it, or one wave for at most 64
+// tokens).  Each workgroup publishes its ids: thread 0 issues an agent-scope
+// release fence (the barrier before it makes the other waves' stores part of
+// it) and increments a device-scope counter; the workgroup that takes the
+// counter to the grid size is the last one, and after thread 0's acquire
+// fence (then the barrier) it sees every token's ids and builds the
+// permutation.  Release and acquire are one L2 write-back and one L2
+// invalidation; a sequentially consistent fence does both, in every
+// workgroup (decode step 397.2 -> 395.9 us).  The counter is set to zero by
+// the router kernel earlier on the same stream.  The permutation depends
+// only on the ids, so it is the same whichever workgroup is last.
 // ---------------------------------------------------------------------------
 constexpr int TOPK_PER_WG = 4;
 
@@ -680,13 +758,17 @@ __global__ __launch_bounds__(1024) void topk_perm_kernel(const float *__restrict
         topk_token<SLOTS, NSP>(zp, splits, bias, T, E, K, t, sel_e_s[wave], sel_z_s[wave], ids, w);
     __syncthreads();                              // this workgroup's ids are written
     if (threadIdx.x == 0) {
-        __threadfence();                          // release them device-wide
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         last_s = atomicAdd(done, 1) == (int)gridDim.x - 1;
+        if (last_s) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!last_s) return;
-    __threadfence();                              // acquire: every workgroup's ids
-    perm_small_body(ids, T, E, K, count, offset, perm, inv);
+    if (T <= PERM_WAVE_T) {
+        if (wave == 0) perm_wave_body(ids, T, E, K, count, offset, perm, inv);
+    } else {
+        perm_small_body(ids, T, E, K, count, offset, perm, inv);
+    }
 }
 
 // ---------------------------------------------------------------------------
