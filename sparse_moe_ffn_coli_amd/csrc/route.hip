@@ -510,11 +510,14 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restric
                                                  __popcll(masks[2 * E + e]) + __popcll(masks[3 * E + e]);
 }
 
-// Every workgroup first forms its tile's first row per expert from the
-// counts of all tiles: offset[e] (exclusive scan over experts of the totals)
-// plus the expert's rows in earlier tiles.  Thread i holds experts 4 i ..
-// 4 i + 3 (E <= 1024); workgroup 0 also writes count and offset.  Then the
-// tile's masks are rebuilt and every assignment is written to its row.
+// Every workgroup forms its tile's first row per expert from the counts of
+// all tiles: offset[e] (exclusive scan over experts of the totals) plus the
+// expert's rows in earlier tiles.  Thread i holds experts 4 i .. 4 i + 3
+// (E <= 1024); workgroup 0 also writes count and offset.  Then every
+// assignment of the tile is written to its row.  The tile's ids are loaded
+// first and every tile's counts right after them (16 tiles per round), so
+// the loads cost one memory latency, and the masks are built from the ids
+// already in registers (prefill permutation stage 16.4 -> 14.9 us, A/B).
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__restrict__ ids, int T, int E,
                                                            int K, const int32_t *__restrict__ tile_count,
                                                            int ntiles, int32_t *__restrict__ count,
@@ -525,18 +528,23 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
     __shared__ uint64_t masks[4 * TOPK_MAX_E];
     __shared__ int32_t first_s[TOPK_MAX_E];
     __shared__ int32_t ws[4];
-    const int tid = threadIdx.x;
+    constexpr int TPR = 16;                       // tiles' counts per round of loads
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t = blockIdx.x * PERM_TILE + tid;
+    int ev[8];
+    load_token_ids(ids, min(t, T - 1), K, ev);
+    for (int i = tid; i < 4 * E; i += PERM_TILE) masks[i] = 0ull;
     int tot[4] = {0, 0, 0, 0}, before[4] = {0, 0, 0, 0};
-    // eight tiles' counts at a time, unconditional loads of clamped indices
-    for (int tl0 = 0; tl0 < ntiles; tl0 += 8) {
-        int v[8][4];
+    // unconditional loads of clamped indices
+    for (int tl0 = 0; tl0 < ntiles; tl0 += TPR) {
+        int v[TPR][4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < TPR; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 v[k][i] = tile_count[(size_t)min(tl0 + k, ntiles - 1) * E + min(4 * tid + i, E - 1)];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < TPR; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tl = tl0 + k;
@@ -550,7 +558,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
         if (4 * tid + i >= E) tot[i] = 0;
         local += tot[i];
     }
-    const int incl = block_scan_incl<4>(local, ws);
+    const int incl = block_scan_incl<4>(local, ws);   // its barriers also order the masks' zeroing
     int run = incl - local;                       // rows of the experts before 4 tid
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -565,13 +573,14 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
         run += tot[i];
     }
     if (blockIdx.x == 0 && tid == 255) offset[E] = incl;
-    build_tile_masks(ids, T, E, K, masks);        // its barriers also publish first_s
-    const int wave = tid >> 6, lane = tid & 63;
-    const int t = blockIdx.x * PERM_TILE + tid;
+    if (t < T) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < K) atomicOr((unsigned long long *)&masks[wave * E + ev[j]], 1ull << lane);
+    }
+    __syncthreads();                              // masks and first_s
     if (t >= T) return;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int ev[8];
-    load_token_ids(ids, t, K, ev);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (j >= K) break;
