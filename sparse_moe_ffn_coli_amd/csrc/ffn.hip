@@ -1085,9 +1085,13 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// row-light tiles: 32 rows x 128 columns (64 h columns per gate+up tile),
-// four workgroups per CU
-using SmallGuCfg = TileCfg<32, 128, 1, 4>;
+// row-light tiles: gate+up 32 rows x 256 weight rows (128 h columns, two
+// workgroups per CU), down 32 x 128 (four per CU).  The wider gate+up tile
+// pays its set-up (tile search, token rows, first stage) once per twice the
+// weight bytes (decode gate+up 249.4 -> 246.6 us, A/B); the same width for
+// down, whose 12-step reductions leave fewer stages in flight per CU at two
+// workgroups, was slower (129.8 -> 132.3 us).
+using SmallGuCfg = TileCfg<32, 256, 1, 4>;
 using SmallDownCfg = TileCfg<32, 128, 1, 4>;
 constexpr int SMALL_BM = SmallGuCfg::BM;
 constexpr int I4N_MAX_T = 128;    // int4 batches up to this size run the narrow engine
