@@ -1094,13 +1094,20 @@ __global__ void combine_f32_kernel(const float *__restrict__ h, const float *__r
 // launchers
 // ---------------------------------------------------------------------------
 // row-light tiles: gate+up 32 rows x 256 weight rows (128 h columns, two
-// workgroups per CU), down 32 x 128 (four per CU).  The wider gate+up tile
-// pays its set-up (tile search, token rows, first stage) once per twice the
-// weight bytes (decode gate+up 249.4 -> 246.6 us, A/B); the same width for
-// down, whose 12-step reductions leave fewer stages in flight per CU at two
-// workgroups, was slower (129.8 -> 132.3 us).
-using SmallGuCfg = TileCfg<32, 256, 1, 4>;
+// workgroups per CU) for batches of at most GU_WIDE_MAX_T tokens that still
+// give at least GU_WIDE_MIN_TILES tiles, else 32 x 128 (64 h columns, four
+// per CU); down 32 x 128.  Measured A/B on one box, gate+up median: wide
+// against narrow 167.0 / 170.9 us at T = 32, 246.8 / 248.3 at T = 64
+// (decode), but 298.5 / 285.5 at T = 96, 304.5 / 294.1 at T = 128 and
+// 313.9 / 306.1 at T = 256; with few tiles (a dense layer of 64 tokens: 108
+// of them) the wide tile leaves CUs idle (dense decode 42 -> 46 us).  The
+// same width for down, whose 12-step reductions leave fewer stages in
+// flight per CU at two workgroups, was slower (129.8 -> 132.3 us at T = 64).
+using SmallGuCfg = TileCfg<32, 128, 1, 4>;
+using SmallGuWideCfg = TileCfg<32, 256, 1, 4>;
 using SmallDownCfg = TileCfg<32, 128, 1, 4>;
+constexpr long GU_WIDE_MIN_TILES = 1024;
+constexpr int GU_WIDE_MAX_T = 64;
 constexpr int SMALL_BM = SmallGuCfg::BM;
 constexpr int I4N_MAX_T = 128;    // int4 batches up to this size run the narrow engine
 constexpr int BIG_BM = BigCfg::BM;
@@ -1261,7 +1268,12 @@ hipError_t launch_ffn(const FfnLaunch &a, hipStream_t st)
             else
                 launch_staged_int4<I4Cfg<64>>(a, mk, st);
         } else if (a.bm == SMALL_BM) {
-            launch_staged<SmallGuCfg, SmallDownCfg>(a, mk, st);
+            // tile count bound: row tiles (at most) x column tiles of the wide tile
+            const long wide_tiles = ffn_max_tiles(a.T, a.E, a.K, SMALL_BM) *
+                                    ((a.F + SmallGuWideCfg::BN / 2 - 1) / (SmallGuWideCfg::BN / 2));
+            if (a.T <= GU_WIDE_MAX_T && wide_tiles >= GU_WIDE_MIN_TILES)
+                launch_staged<SmallGuWideCfg, SmallDownCfg>(a, mk, st);
+            else launch_staged<SmallGuCfg, SmallDownCfg>(a, mk, st);
         } else {
             launch_big(a, mk, st);
         }
