@@ -161,12 +161,16 @@ def test_int4_narrow_engine(cid, T, D, E, K, F):
 
 # bf16 routed batches on the row-light tiles (R <= 24 E): 160 about 21 rows per
 # expert, 161 a single token at the workload widths, 162 K = 4, 163 128 tokens
-# over 288 experts
+# over 288 experts; 164 and 165 take the 32 x 256 gate+up tiles (at most 64
+# tokens, at least 1024 tiles), 165 with F = 704, whose last column tile holds
+# 64 of its 128 h columns
 @pytest.mark.parametrize("cid,T,D,E,K,F", [
     (160, 128, 256, 48, 8, 256),
     (161, 1, 2048, 288, 8, 768),
     (162, 90, 512, 64, 4, 384),
     (163, 128, 1024, 288, 8, 512),
+    (164, 32, 1024, 288, 8, 768),
+    (165, 48, 256, 288, 8, 704),
 ])
 def test_bf16_row_light_batches(cid, T, D, E, K, F):
     cfg = custom_cfg(cid, T, D, E, K, F, "bf16")
@@ -212,6 +216,10 @@ def test_int4_small_scales(cid, F):
     # fp32 above the fused top-K + permutation path: the fp32 router zeroes the
     # per-tile counts that the top-K kernel accumulates
     (120, 1100, 64, 40, 8, 64, "f32"),
+    # the one-wave permutation of at most 64 tokens at the largest E it takes
+    # (eight experts per lane), and one token past it (the 16-wave one)
+    (121, 64, 128, 512, 8, 64, "bf16"),
+    (122, 65, 128, 288, 8, 64, "bf16"),
 ])
 def test_edge_shapes(cid, T, D, E, K, F, dt):
     cfg = custom_cfg(cid, T, D, E, K, F, dt)
