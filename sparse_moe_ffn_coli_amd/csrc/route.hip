@@ -386,30 +386,47 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ zp, int spl
         // padding slot (image 0) is never among the K taken below
         key[s] = (lane + 64 * s < E) ? max(ordered_bits(v + bs[s]), 1u) : 0u;
     }
-    // the K largest images one per round: the wave maximum m of the images
-    // not yet taken, then the lowest expert index holding m (slots, then
-    // lanes, ascending) is taken.  Equal images therefore go to the lower
-    // index, and the K taken are the first K of the order (image desc, index asc).
-    uint64_t chosen[SLOTS];
-    uint32_t rem[SLOTS];
+    // The K largest images, ties to the lower expert index.  First the K
+    // largest lane maxima, one per round (wave maximum of the lanes' heads,
+    // one lane holding it retired); tau, the K-th of them, is a lower bound
+    // of the K-th largest image, since K distinct lanes hold an image >= tau,
+    // so every image of the top K is >= tau.  The candidates (images >= tau;
+    // padding slots are 0 < tau) are exactly the top K unless some lane holds
+    // two of them or images tie at tau; then the smallest candidates --
+    // image ascending, expert index descending -- are dropped one per round
+    // until K remain, leaving the first K of the order (image desc, index asc).
+    uint32_t head = key[0];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) { chosen[s] = 0ull; rem[s] = key[s]; }
+    for (int s = 1; s < SLOTS; ++s) head = max(head, key[s]);
+    uint32_t tau = 0;
     for (int j = 0; j < K; ++j) {
-        uint32_t m = rem[0];
+        const uint32_t m = wave_max_u32(head);
+        tau = m;
+        const uint64_t b = __ballot(head == m);
+        if (lane == __ffsll((unsigned long long)b) - 1) head = 0u;
+    }
+    uint64_t chosen[SLOTS];
+    int ncand = 0;
 #pragma unroll
-        for (int s = 1; s < SLOTS; ++s) m = max(m, rem[s]);
-        m = wave_max_u32(m);
-        bool taken = false;
+    for (int s = 0; s < SLOTS; ++s) {
+        chosen[s] = __ballot(key[s] >= tau);
+        ncand += __popcll(chosen[s]);
+    }
+    while (ncand > K) {
+        uint32_t mn = 0xffffffffu;                // smallest candidate of this lane
 #pragma unroll
-        for (int s = 0; s < SLOTS; ++s) {
-            const uint64_t b = __ballot(rem[s] == m);
-            if (!taken && b) {
-                const uint64_t low = b & (~b + 1);   // lowest set bit
-                chosen[s] |= low;
-                if ((low >> lane) & 1ull) rem[s] = 0u;
-                taken = true;
+        for (int s = 0; s < SLOTS; ++s)
+            if ((chosen[s] >> lane) & 1ull) mn = min(mn, key[s]);
+        mn = wave_reduce_u32(mn, MinU32());
+#pragma unroll
+        for (int s = SLOTS - 1; s >= 0; --s) {    // highest expert index holding it
+            const uint64_t b = chosen[s] & __ballot(key[s] == mn);
+            if (b) {
+                chosen[s] &= ~(1ull << (63 - __clzll((long long)b)));
+                break;
             }
         }
+        --ncand;
     }
     // output position of each chosen expert: chosen experts of lower slots,
     // then lower lanes of this slot
