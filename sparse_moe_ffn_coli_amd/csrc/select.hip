@@ -408,14 +408,231 @@ __global__ __launch_bounds__(SEL_NT) void index_topk_long_kernel(const float *__
                     idx + (size_t)r * k);
 }
 
+// ---- rows of up to SEL_CAP positions, keys held in registers ---------------
+// For launches with more rows than CUs.  One workgroup of 8 waves per row,
+// two workgroups per CU (two rows in flight, each with half the waves of a
+// cached-row workgroup at its barriers, and no 128 KB key array in LDS).
+// Thread t holds the groups of four positions 4 (j * SR_NT + t) .. + 3,
+// j < SR_PER, as keys in registers, so the radix passes and the compaction
+// read no keys from LDS.  Same selection as the cached kernel: the k-th
+// largest key tau by three radix digits, every key above tau, and of those
+// equal to tau the lowest positions; the output in ascending position order.
+// (2048 rows of 30 721-32 768 scores: 179 -> 153 us.  With 1024 threads and
+// 32 keys each the registers spill heavily (301 us); four histogram copies
+// indexed by lane, against same-address atomics, measured the same.)
+constexpr int SR_NT = 512;
+constexpr int SEL_REG_MIN_ROWS = 256;    // larger launches run index_topk_reg_kernel
+constexpr int SR_WAVES = SR_NT / 64;
+constexpr int SR_PER = SEL_CAP / (4 * SR_NT);     // groups of four positions per thread
+static_assert(SR_WAVES % 4 == 0 && 4 * SR_NT >= 2048, "wave totals in fours; four bins per thread");
+
+// Inclusive prefix sum over the workgroup in thread order (ws: SR_WAVES ints).
+__device__ __forceinline__ int sr_block_scan_incl(int v, int32_t *ws)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_scan_incl(v);
+    if (lane == 63) ws[wave] = v;
+    lds_barrier();
+    int before = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < SR_WAVES; ++w2) before += (w2 < wave) ? ws[w2] : 0;
+    return v + before;
+}
+
+// The digit holding the need-th largest key among bins 0 .. nb - 1 (nb <=
+// 4 * SR_NT): thread t holds bins nb-1-4t .. nb-4-4t, so a scan in thread
+// order is a suffix scan over the bins.  Returns the bin; *above receives the
+// keys in higher bins.  Clears the bins it read.  The caller's next write of
+// ws or sel_s comes after another barrier.
+__device__ __forceinline__ int sr_pick_bin(int32_t *hist, int nb, int need, int32_t *ws, int32_t *sel_s,
+                                           int *above_out)
+{
+    const int tid = threadIdx.x;
+    int c[4], sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = nb - 1 - 4 * tid - u;
+        c[u] = (b >= 0) ? hist[b] : 0;
+        sum += c[u];
+    }
+    int acc = sr_block_scan_incl(sum, ws) - sum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (acc < need && acc + c[u] >= need) {
+            sel_s[0] = nb - 1 - 4 * tid - u;
+            sel_s[1] = acc;
+        }
+        acc += c[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = nb - 1 - 4 * tid - u;
+        if (b >= 0) hist[b] = 0;
+    }
+    lds_barrier();
+    *above_out = sel_s[1];
+    return sel_s[0];
+}
+
+__global__ __launch_bounds__(SR_NT) __attribute__((amdgpu_waves_per_eu(SR_NT / 128))) void index_topk_reg_kernel(
+    const float *__restrict__ scores, int L, long ld, const int32_t *__restrict__ lens, int k, int tail,
+    int32_t *__restrict__ idx)
+{
+    __shared__ int32_t hist[2048];
+    __shared__ int32_t ws[SR_WAVES];
+    __shared__ int32_t sel_s[2];
+    __shared__ __attribute__((aligned(16))) int32_t tot[SR_PER][SR_WAVES];    // per group round, per wave
+    __shared__ __attribute__((aligned(16))) int32_t staged[SEL_MAX_K];        // the output row
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lens ? min(max(lens[r], 0), L) : L;
+    int32_t *__restrict__ out = idx + (size_t)r * k;
+    if (n <= k) {                                 // the whole row, then -1
+        for (int j = tid; j < k; j += SR_NT) out[j] = j < n ? j : -1;
+        return;
+    }
+    if (n > SEL_CAP) return;                      // index_topk_long_kernel's row
+    const float *__restrict__ row = scores + (size_t)r * ld;
+    const int tail0 = n - min(tail, k);           // positions >= tail0 are always kept
+    const int n4 = n & ~3;
+
+    // the row's scores: 16-byte buffer loads of whole groups (the buffer
+    // ends after the last whole group, so the loads past it return zeros and
+    // need no clamped addresses), then the last 0-3 positions one by one
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), 0, n4 * 4, 0x00020000);
+    f32x4 v[SR_PER];
+#pragma unroll
+    for (int j = 0; j < SR_PER; ++j)
+        v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * tid, 16 * j * SR_NT, 0));
+    // the last 0-3 positions: group n4 / 4, i.e. round jt of thread tt
+    const int g4 = n4 >> 2, jt = g4 / SR_NT, tt = g4 - jt * SR_NT;
+    float ex[3] = {0.f, 0.f, 0.f};
+    if (tid == tt) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+            if (n4 + c < n) ex[c] = row[n4 + c];
+    }
+    for (int b = tid; b < 2048; b += SR_NT) hist[b] = 0;
+    uint32_t q[SR_PER][4];
+#pragma unroll
+    for (int j = 0; j < SR_PER; ++j) {
+        const int p0 = 4 * (j * SR_NT + tid);
+        const bool last = j == jt && tid == tt;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) v[j][c] = last ? ex[c] : v[j][c];
+        // positions past the row take key 0, below every real key but one
+        // that a real key can share: the histograms discount them (bin 0,
+        // while the digits found so far are all 0), and as they follow every
+        // real position the compaction never reaches them
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            q[j][c] = (p0 + c >= n) ? 0u : (p0 + c >= tail0) ? 0xffffffffu : score_key(v[j][c]);
+    }
+    const int pad = SEL_CAP - n;                  // positions past the row
+    lds_barrier();                                // hist is clear
+
+    // radix select: digits of 11, 11 and 10 bits, most significant first
+#pragma unroll
+    for (int j = 0; j < SR_PER; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) atomicAdd(&hist[q[j][c] >> 21], 1);
+    if (tid == 0) atomicAdd(hist, -pad);
+    lds_barrier();
+    int need = k, above;
+    uint32_t prefix = (uint32_t)sr_pick_bin(hist, 2048, need, ws, sel_s, &above) << 21;
+    need -= above;
+#pragma unroll 1
+    for (int pass = 1; pass < 3; ++pass) {
+        const int shift = pass == 1 ? 10 : 0;
+        const int nb = pass == 2 ? 1024 : 2048;
+        const uint32_t hi = 0xffffffffu << (shift + (pass == 2 ? 10 : 11));
+#pragma unroll
+        for (int j = 0; j < SR_PER; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if ((q[j][c] & hi) == prefix) atomicAdd(&hist[(q[j][c] >> shift) & (nb - 1)], 1);
+        if (tid == 0 && prefix == 0u) atomicAdd(hist, -pad);
+        lds_barrier();
+        prefix |= (uint32_t)sr_pick_bin(hist, nb, need, ws, sel_s, &above) << shift;
+        need -= above;
+    }
+    const uint32_t tau = prefix;
+
+    // ordered compaction: per group round j, the keys above tau (low 16 bits)
+    // and equal to tau (high 16 bits) of this thread, scanned over the wave;
+    // the wave totals of every round go through LDS in one barrier
+    // (packed sums stay below 2^32: at most SEL_CAP keys in each half; the
+    // scans are recomputed after the barrier rather than kept in registers)
+    auto round_count = [&](int j) {
+        int cnt = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            cnt += (q[j][c] > tau) ? 1 : 0;
+            cnt += (q[j][c] == tau) ? 0x10000 : 0;
+        }
+        return cnt;
+    };
+#pragma unroll
+    for (int j = 0; j < SR_PER; ++j) {
+        const int incl = wave_scan_incl(round_count(j));   // at most 256 per half
+        if (lane == 63) tot[j][wave] = incl;
+    }
+    lds_barrier();
+    uint32_t base = 0;                            // packed counts of all rounds before j
+#pragma unroll
+    for (int j = 0; j < SR_PER; ++j) {
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (int w4 = 0; w4 < SR_WAVES; w4 += 4) {
+            const int4 t4 = *reinterpret_cast<const int4 *>(&tot[j][w4]);
+            const uint32_t tw[4] = {(uint32_t)t4.x, (uint32_t)t4.y, (uint32_t)t4.z, (uint32_t)t4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                before += (w4 + u < wave) ? tw[u] : 0u;
+                all += tw[u];
+            }
+        }
+        const int cnt = round_count(j);
+        uint32_t my = base + before + (uint32_t)(wave_scan_incl(cnt) - cnt);
+        const int p0 = 4 * (j * SR_NT + tid);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int gt = (int)(my & 0xffffu), eq = (int)(my >> 16);
+            if (q[j][c] > tau) {
+                staged[gt + min(eq, need)] = p0 + c;
+                my += 1u;
+            } else if (q[j][c] == tau) {
+                if (eq < need) staged[gt + eq] = p0 + c;
+                my += 0x10000u;
+            }
+        }
+        base += all;
+    }
+    lds_barrier();
+    if ((k & 3) == 0) {
+        for (int j = 4 * tid; j < k; j += 4 * SR_NT)
+            *reinterpret_cast<u32x4 *>(out + j) = *reinterpret_cast<const u32x4 *>(staged + j);
+    } else {
+        for (int j = tid; j < k; j += SR_NT) out[j] = staged[j];
+    }
+}
+
 hipError_t launch_index_topk(const float *scores, int rows, int L, long ld, const int32_t *lens, int k, int tail,
                              int32_t *idx, hipStream_t st)
 {
     if (rows == 0) return hipSuccess;
-    // one workgroup per CU (the key cache fills most of a CU's LDS), each
-    // walking its share of the rows
-    const int grid = min(rows, 256);
-    index_topk_kernel<<<grid, SEL_NT, 0, st>>>(scores, rows, L, ld, lens, k, tail, idx);
+    // more rows than CUs: the register-key kernel; otherwise one workgroup
+    // per CU (the key cache fills most of a CU's LDS), each walking its
+    // share of the rows
+    if (rows > SEL_REG_MIN_ROWS) {
+        // two rows in flight per CU (64 rows: 28.2 us here against 24.4 us
+        // for one cached-row workgroup per CU, each row's latency deciding)
+        index_topk_reg_kernel<<<rows, SR_NT, 0, st>>>(scores, L, ld, lens, k, tail, idx);
+    } else {
+        const int grid = min(rows, 256);
+        index_topk_kernel<<<grid, SEL_NT, 0, st>>>(scores, rows, L, ld, lens, k, tail, idx);
+    }
     if (L > SEL_CAP && L > k) index_topk_long_kernel<<<rows, SEL_NT, 0, st>>>(scores, L, ld, lens, k, tail, idx);
     return hipGetLastError();
 }

@@ -77,3 +77,42 @@ def test_index_topk_workloads_every_row(name):
     cfg = synth.INDEX_CONFIGS[name]
     s, lens = synth.index_scores(cfg)
     _check(s, cfg["k"], cfg["tail"], lens, label=name)
+
+
+# Launches with more rows than CUs run the register-key kernel: the same
+# cases at 260-300 rows.
+@pytest.mark.parametrize("rows,L,k,tail,ties", [
+    (300, 100, 16, 0, True),
+    (260, 257, 64, 4, True),
+    (257, 32768, 2048, 4, True),
+    (260, 32765, 2048, 4, False),
+    (260, 5000, 4096, 3, False),
+    (260, 3000, 1, 0, True),
+    (260, 3000, 2, 5, False),
+    (260, 7, 3, 1, False),
+])
+def test_index_topk_many_rows(rows, L, k, tail, ties):
+    rng = np.random.default_rng(rows * 7 + L)
+    s = (rng.integers(0, 7, size=(rows, L)) if ties else rng.standard_normal((rows, L))).astype(np.float32)
+    _check(s, k, tail, label=f"rows={rows} L={L} k={k} tail={tail}")
+
+
+def test_index_topk_many_rows_lengths():
+    # lengths from empty to past the cached limit in one launch
+    rng = np.random.default_rng(11)
+    rows, L, k = 300, 40000, 2048
+    s = rng.standard_normal((rows, L)).astype(np.float32)
+    lens = rng.integers(0, L + 1, size=rows).astype(np.int32)
+    lens[:12] = [0, 1, 3, 2047, 2048, 2049, 2050, 2051, 32767, 32768, 32769, 40000]
+    _check(s, k, 4, lens, label="many rows, mixed lengths")
+
+
+def test_index_topk_many_rows_special_values():
+    rows, L = 270, 300
+    s = np.zeros((rows, L), np.float32)
+    s[0::3, ::2] = -0.0
+    s[1::3, :] = -np.inf
+    s[1::3, 7] = np.inf
+    s[2::3, :] = np.float32(1e-45)
+    s[2::3, 50:60] = -np.float32(1e-45)
+    _check(s, 37, 0, label="many rows: signed zeros / infinities / subnormals")
